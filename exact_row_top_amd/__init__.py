@@ -1,0 +1,225 @@
+"""Exact per-row top-K for MI355X (gfx950): thin Python binding of the C ABI.
+
+Every step of the selection runs in the HIP kernels of ``libexact_row_top.so``;
+this module only marshals torch tensors (device memory and the current HIP
+stream) into the C calls declared in ``include/exact_row_top.h``.  There is no
+CPU fallback: if the library is missing or the device is not gfx950 the calls
+raise.
+
+    out = topk_decode(logits, n_valid, k)               # logits [rows, stride] fp32
+    out = topk_prefill(logits, row_starts, row_ends, k)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libexact_row_top.so")
+
+TOPK_OK, TOPK_EINVAL, TOPK_ELAYOUT, TOPK_EWORKSPACE, TOPK_EDEVICE, TOPK_ELAUNCH = range(6)
+STATS_WORDS = 8
+VALID_K = (512, 1024, 2048)
+
+_lib = None
+
+
+class TopKError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"exact_row_top status {status}: {msg}")
+        self.status = status
+
+
+class _Options(ctypes.Structure):
+    _fields_ = [("force_wgs_per_row", ctypes.c_int32),
+                ("force_rescue", ctypes.c_int32),
+                ("row_stats", ctypes.c_void_p)]
+
+
+def load_library():
+    """Load the C ABI library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m exact_row_top_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.topk_decode.argtypes = [P, I64, P, I32, I32, P, P, SZ, P]
+    lib.topk_decode.restype = ctypes.c_int
+    lib.topk_prefill.argtypes = [P, I64, P, P, I32, I32, P, I64, P, SZ, P]
+    lib.topk_prefill.restype = ctypes.c_int
+    lib.topk_decode_ex.argtypes = [P, I64, P, I32, I32, P, P, SZ, P, ctypes.POINTER(_Options)]
+    lib.topk_decode_ex.restype = ctypes.c_int
+    lib.topk_prefill_ex.argtypes = [P, I64, P, P, I32, I32, P, I64, P, SZ, P,
+                                    ctypes.POINTER(_Options)]
+    lib.topk_prefill_ex.restype = ctypes.c_int
+    lib.topk_workspace_bytes.argtypes = [I32, I64, I32]
+    lib.topk_workspace_bytes.restype = SZ
+    lib.topk_workspace_init.argtypes = [P, SZ, P]
+    lib.topk_workspace_init.restype = ctypes.c_int
+    lib.topk_strerror.argtypes = [ctypes.c_int]
+    lib.topk_strerror.restype = ctypes.c_char_p
+    lib.topk_plan_query.argtypes = [I32, I64, I64, I32, I32, I32, I32, ctypes.POINTER(I64)]
+    lib.topk_plan_query.restype = ctypes.c_int
+    lib.topk_validate.argtypes = [I32, P, I64, P, P, I32, I32, P, P, SZ, I64]
+    lib.topk_validate.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def strerror(status: int) -> str:
+    return load_library().topk_strerror(int(status)).decode()
+
+
+def _check(status: int):
+    if status != TOPK_OK:
+        raise TopKError(status, strerror(status))
+
+
+def workspace_bytes(num_rows: int, row_stride: int, k: int) -> int:
+    return int(load_library().topk_workspace_bytes(int(num_rows), int(row_stride), int(k)))
+
+
+def plan_query(num_rows: int, row_stride: int, k: int, force_wgs_per_row: int = 0,
+               cu_count: int = 256, wgs_per_cu: int = 2) -> dict:
+    """The launch plan the library would use (host-only, no GPU needed)."""
+    out = (ctypes.c_int64 * 6)()
+    _check(load_library().topk_plan_query(num_rows, row_stride, 0, k, force_wgs_per_row,
+                                          cu_count, wgs_per_cu, out))
+    keys = ("wgs_per_row", "quads_per_thread", "rows_per_launch", "launches", "workspace_bytes", "cap")
+    return dict(zip(keys, (int(x) for x in out)))
+
+
+# ---------------------------------------------------------------------------
+# torch marshalling
+# ---------------------------------------------------------------------------
+
+def _stream_ptr(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) or None
+
+
+def _require(t, name, dtype, ndim=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-D")
+
+
+def _logits_layout(logits):
+    import torch
+    _require(logits, "logits", torch.float32, 2)
+    if logits.stride(1) != 1:
+        raise ValueError("logits must have unit inner stride")
+    rows = logits.shape[0]
+    row_stride = logits.stride(0) if rows > 1 else logits.shape[1]
+    if rows > 1 and row_stride < logits.shape[1]:
+        raise ValueError("logits rows overlap")
+    # the kernel may read any aligned float4 of a row's full stride
+    need = (logits.storage_offset() + rows * row_stride) * 4
+    if rows and logits.untyped_storage().nbytes() < need:
+        raise ValueError("logits storage must hold rows x row_stride floats (full last row)")
+    return rows, int(row_stride)
+
+
+def _out(indices, rows, k, device):
+    import torch
+    if indices is None:
+        return torch.empty((rows, k), dtype=torch.int32, device=device)
+    _require(indices, "indices", torch.int32, 2)
+    if tuple(indices.shape) != (rows, k) or not indices.is_contiguous():
+        raise ValueError(f"indices must be a contiguous int32 [{rows}, {k}] tensor")
+    return indices
+
+
+def _opts(force_wgs_per_row, force_rescue, row_stats, rows):
+    import torch
+    if not (force_wgs_per_row or force_rescue or row_stats is not None):
+        return None
+    if row_stats is not None:
+        _require(row_stats, "row_stats", torch.int32, 2)
+        if tuple(row_stats.shape) != (rows, STATS_WORDS) or not row_stats.is_contiguous():
+            raise ValueError(f"row_stats must be a contiguous int32 [{rows}, {STATS_WORDS}] tensor")
+    o = _Options(int(force_wgs_per_row), int(bool(force_rescue)),
+                 row_stats.data_ptr() if row_stats is not None else None)
+    return ctypes.pointer(o)
+
+
+def _ws(workspace):
+    if workspace is None:
+        return None, 0
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def topk_decode(logits, n_valid, k: int, indices=None, *, workspace=None, stream=None,
+                force_wgs_per_row: int = 0, force_rescue: bool = False, row_stats=None):
+    """Exact top-k of logits[r, :n_valid[r]] per row (local indices, -1 pad)."""
+    import torch
+    lib = load_library()
+    rows, row_stride = _logits_layout(logits)
+    _require(n_valid, "n_valid", torch.int32, 1)
+    if n_valid.shape[0] != rows or not n_valid.is_contiguous():
+        raise ValueError("n_valid must be a contiguous int32 [rows] tensor")
+    out = _out(indices, rows, k, logits.device)
+    wp, wb = _ws(workspace)
+    opts = _opts(force_wgs_per_row, force_rescue, row_stats, rows)
+    s = _stream_ptr(stream)
+    if opts is None:
+        rc = lib.topk_decode(logits.data_ptr(), row_stride, n_valid.data_ptr(), rows, k,
+                             out.data_ptr(), wp, wb, s)
+    else:
+        rc = lib.topk_decode_ex(logits.data_ptr(), row_stride, n_valid.data_ptr(), rows, k,
+                                out.data_ptr(), wp, wb, s, opts)
+    _check(rc)
+    return out
+
+
+def topk_prefill(logits, row_starts, row_ends, k: int, indices=None, *, max_row_len: int = 0,
+                 workspace=None, stream=None, force_wgs_per_row: int = 0,
+                 force_rescue: bool = False, row_stats=None):
+    """Exact top-k of logits[r, row_starts[r]:row_ends[r]] per row (ks-relative)."""
+    import torch
+    lib = load_library()
+    rows, row_stride = _logits_layout(logits)
+    for name, t in (("row_starts", row_starts), ("row_ends", row_ends)):
+        _require(t, name, torch.int32, 1)
+        if t.shape[0] != rows or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 [rows] tensor")
+    out = _out(indices, rows, k, logits.device)
+    wp, wb = _ws(workspace)
+    opts = _opts(force_wgs_per_row, force_rescue, row_stats, rows)
+    s = _stream_ptr(stream)
+    if opts is None:
+        rc = lib.topk_prefill(logits.data_ptr(), row_stride, row_starts.data_ptr(),
+                              row_ends.data_ptr(), rows, k, out.data_ptr(), int(max_row_len),
+                              wp, wb, s)
+    else:
+        rc = lib.topk_prefill_ex(logits.data_ptr(), row_stride, row_starts.data_ptr(),
+                                 row_ends.data_ptr(), rows, k, out.data_ptr(), int(max_row_len),
+                                 wp, wb, s, opts)
+    _check(rc)
+    return out
+
+
+def new_workspace(num_rows: int, row_stride: int, k: int, device="cuda", stream=None):
+    """Allocate and zero a caller-owned workspace (None when the plan needs none)."""
+    import torch
+    nbytes = workspace_bytes(num_rows, row_stride, k)
+    if nbytes == 0:
+        return None
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    _check(load_library().topk_workspace_init(ws.data_ptr(), nbytes, _stream_ptr(stream)))
+    return ws
+
+
+__all__ = ["topk_decode", "topk_prefill", "workspace_bytes", "new_workspace", "plan_query",
+           "strerror", "load_library", "TopKError", "STATS_WORDS", "VALID_K"]

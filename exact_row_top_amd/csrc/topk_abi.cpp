@@ -1,0 +1,349 @@
+// topk_abi.cpp -- C ABI of the exact per-row top-K library: host-side
+// validation (no device reads), launch planning, workspace ownership and the
+// kernel launches.  The contract is documented in include/exact_row_top.h.
+
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <string.h>
+
+#include "exact_row_top.h"
+#include "gvr_common.h"
+
+namespace ert {
+const void* gvr_kernel(int k, int qpt, bool split);
+}
+
+using namespace ert;
+
+namespace {
+
+bool k_ok(int32_t k) { return k == 512 || k == 1024 || k == 2048; }
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+struct Plan {
+  int G = 1;             // workgroups per row
+  int qpt = 4;           // float4 groups per thread
+  int rows_per_launch = 0;
+  int launches = 0;
+  size_t ws_bytes = 0;
+  int cap = kSingleCap;  // candidate cap
+  int xcd_group = 0;
+};
+
+int64_t quads_for(int64_t env_len) {
+  // A window of env_len floats starting at any ks spans at most this many
+  // aligned float4 groups (lead <= 3 plus a partial last group).
+  return (env_len + 3 + 3) / 4;
+}
+
+int smallest_qpt(int64_t quads_per_part) {
+  for (int q : kQptList)
+    if ((int64_t)kBlock * q >= quads_per_part) return q;
+  return 0;
+}
+
+// Launch shape for (rows, envelope, k).  `capacity` = workgroups the device
+// keeps resident at once for the split kernel (only the split tier needs its
+// workgroups co-resident, for its row barriers).
+int make_plan(int32_t num_rows, int64_t env_len, int32_t k, int32_t force_g, int64_t capacity,
+              Plan* pl) {
+  Plan p;
+  const int64_t Qmax = quads_for(env_len < 1 ? 1 : env_len);
+  const int64_t one_wg_quads = (int64_t)kBlock * kQptMax;
+  int G;
+  if (force_g > 0) {
+    if (force_g > kMaxWgsPerRow) return TOPK_EINVAL;
+    G = force_g;
+  } else {
+    const int64_t g_min = (Qmax + one_wg_quads - 1) / one_wg_quads;
+    // aim for ~512 workgroups in flight, but never parts below 4 groups/thread
+    const int64_t target = 512;
+    const int64_t g_fill = (target + num_rows - 1) / (num_rows > 0 ? num_rows : 1);
+    const int64_t g_useful = (Qmax + (int64_t)kBlock * 4 - 1) / ((int64_t)kBlock * 4);
+    int64_t gg = g_fill < g_useful ? g_fill : g_useful;
+    if (gg < g_min) gg = g_min;
+    if (gg < 1) gg = 1;
+    if (gg > kMaxWgsPerRow) return TOPK_EINVAL;  // row longer than the largest plan
+    G = (int)gg;
+  }
+  const int64_t per_part = (Qmax + G - 1) / G;
+  const int qpt = smallest_qpt(per_part);
+  if (qpt == 0) return TOPK_EINVAL;  // forced G too small for this row length
+  p.G = G;
+  p.qpt = qpt;
+  if (G == 1) {
+    p.rows_per_launch = num_rows;
+    p.launches = num_rows > 0 ? 1 : 0;
+    p.ws_bytes = 0;
+    p.cap = kSingleCap;
+  } else {
+    int64_t rpl = capacity / G;
+    if (rpl > kMaxSlots) rpl = kMaxSlots;
+    if (rpl > num_rows) rpl = num_rows;
+    if (rpl < 1) return TOPK_EINVAL;
+    p.rows_per_launch = (int)rpl;
+    p.launches = num_rows > 0 ? (int)((num_rows + rpl - 1) / rpl) : 0;
+    // slots are padded to a multiple of 8 when a row's workgroups share an XCD
+    p.xcd_group = (rpl >= 8) ? 1 : 0;
+    const int64_t slots = p.xcd_group ? ((rpl + 7) / 8) * 8 : rpl;
+    if (p.xcd_group && slots * G > capacity) p.xcd_group = 0;
+    const int64_t nslots = p.xcd_group ? slots : rpl;
+    p.ws_bytes = kWsHeaderBytes + (size_t)nslots * kSlotBytes;
+    int64_t cap = (int64_t)G * kSplitCapPerWg;
+    if (cap > 32LL * k) cap = 32LL * k;
+    if (cap > kSplitCapMax) cap = kSplitCapMax;
+    p.cap = (int)cap;
+  }
+  *pl = p;
+  return TOPK_OK;
+}
+
+// Workspace bytes independent of the device: the largest slot count any
+// device could use (rows per launch is bounded by kMaxSlots and num_rows).
+size_t ws_bytes_upper(int32_t num_rows, int64_t env_len, int32_t k, int32_t force_g) {
+  Plan p;
+  if (make_plan(num_rows, env_len, k, force_g, (int64_t)1 << 40, &p) != TOPK_OK) return 0;
+  if (p.G == 1) return 0;
+  int64_t rpl = num_rows < kMaxSlots ? num_rows : kMaxSlots;
+  int64_t slots = ((rpl + 7) / 8) * 8;
+  return kWsHeaderBytes + (size_t)slots * kSlotBytes;
+}
+
+int validate(int mode, const void* logits, int64_t row_stride, const void* e1, const void* e2,
+             int32_t num_rows, int32_t k, const void* indices, int32_t force_g) {
+  if (num_rows < 0 || !k_ok(k) || row_stride < 1 || force_g < 0 || force_g > kMaxWgsPerRow)
+    return TOPK_EINVAL;
+  if (num_rows == 0) return TOPK_OK;
+  if (!logits || !indices || !e1 || (mode == 1 && !e2)) return TOPK_EINVAL;
+  if (!aligned(logits, 16) || (row_stride % 4) != 0) return TOPK_ELAYOUT;
+  if (!aligned(indices, 4) || !aligned(e1, 4) || (mode == 1 && !aligned(e2, 4))) return TOPK_ELAYOUT;
+  return TOPK_OK;
+}
+
+// ---- per-device facts ------------------------------------------------------
+struct DevInfo {
+  bool probed = false;
+  bool ok = false;
+  int cus = 0;
+  int occ[3][3] = {};  // [k idx][qpt idx] split-kernel workgroups per CU
+  void* slab = nullptr;
+  size_t slab_bytes = 0;
+};
+constexpr int kMaxDev = 64;
+DevInfo g_dev[kMaxDev];
+std::mutex g_mu;
+
+int kidx(int k) { return k == 512 ? 0 : (k == 1024 ? 1 : 2); }
+int qidx(int q) { return q == 4 ? 0 : (q == 8 ? 1 : 2); }
+
+int device_info(DevInfo** out, int* dev_out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return TOPK_EDEVICE;
+  DevInfo& d = g_dev[dev];
+  if (!d.probed) {
+    d.probed = true;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return TOPK_EDEVICE;
+    d.ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    d.cus = prop.multiProcessorCount;
+    for (int ki = 0; ki < 3; ++ki)
+      for (int qi = 0; qi < 3; ++qi) {
+        const int ks[3] = {512, 1024, 2048};
+        int nb = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &nb, gvr_kernel(ks[ki], kQptList[qi], true), kBlock, 0) != hipSuccess)
+          nb = 1;
+        d.occ[ki][qi] = nb > 0 ? nb : 1;
+      }
+  }
+  if (!d.ok) return TOPK_EDEVICE;
+  *out = &d;
+  *dev_out = dev;
+  return TOPK_OK;
+}
+
+int run(int mode, const float* logits, int64_t row_stride, const int32_t* e1, const int32_t* e2,
+        int32_t num_rows, int32_t k, int32_t* indices, int64_t max_row_len, void* workspace,
+        size_t workspace_bytes, hipStream_t stream, const topk_options* opts) {
+  const int32_t force_g = opts ? opts->force_wgs_per_row : 0;
+  int rc = validate(mode, logits, row_stride, e1, e2, num_rows, k, indices, force_g);
+  if (rc != TOPK_OK) return rc;
+  if (opts && opts->row_stats && !aligned(opts->row_stats, 4)) return TOPK_ELAYOUT;
+  if (num_rows == 0) return TOPK_OK;
+  // Plans are sized for the full row stride, so any window inside it fits the
+  // resident capacity; the prefill length hint is accepted but not needed.
+  if (max_row_len < 0) return TOPK_EINVAL;
+  const int64_t env = row_stride;
+
+  std::lock_guard<std::mutex> lock(g_mu);
+  DevInfo* d = nullptr;
+  int dev = 0;
+  rc = device_info(&d, &dev);
+  if (rc != TOPK_OK) return rc;
+
+  // The plan's first guess may be for a single workgroup per row; the split
+  // capacity is only consulted when G > 1.
+  Plan pl;
+  rc = make_plan(num_rows, env, k, force_g, (int64_t)1 << 40, &pl);
+  if (rc != TOPK_OK) return rc;
+  if (pl.G > 1) {
+    const int64_t cap = (int64_t)d->cus * d->occ[kidx(k)][qidx(pl.qpt)];
+    rc = make_plan(num_rows, env, k, force_g, cap, &pl);
+    if (rc != TOPK_OK) return rc;
+  }
+
+  unsigned char* ws = nullptr;
+  if (pl.G > 1) {
+    if (workspace) {
+      if (workspace_bytes < pl.ws_bytes) return TOPK_EWORKSPACE;
+      ws = static_cast<unsigned char*>(workspace);
+    } else {
+      const size_t need = ws_bytes_upper(num_rows, env, k, force_g);
+      const size_t want = need > pl.ws_bytes ? need : pl.ws_bytes;
+      if (d->slab_bytes < want) {
+        if (d->slab) {
+          if (hipDeviceSynchronize() != hipSuccess) return TOPK_ELAUNCH;
+          (void)hipFree(d->slab);
+          d->slab = nullptr;
+          d->slab_bytes = 0;
+        }
+        void* ptr = nullptr;
+        if (hipMalloc(&ptr, want) != hipSuccess) return TOPK_ELAUNCH;
+        if (hipMemsetAsync(ptr, 0, want, stream) != hipSuccess) return TOPK_ELAUNCH;
+        d->slab = ptr;
+        d->slab_bytes = want;
+      }
+      ws = static_cast<unsigned char*>(d->slab);
+    }
+  }
+
+  const void* kern = gvr_kernel(k, pl.qpt, pl.G > 1);
+  if (!kern) return TOPK_EINVAL;
+  GvrParams prm;
+  memset(&prm, 0, sizeof(prm));
+  prm.logits = logits;
+  prm.row_stride = row_stride;
+  prm.n_valid = (mode == 0) ? e1 : nullptr;
+  prm.row_starts = (mode == 1) ? e1 : nullptr;
+  prm.row_ends = (mode == 1) ? e2 : nullptr;
+  prm.wgs_per_row = pl.G;
+  prm.cap = pl.cap;
+  prm.force_rescue = (opts && opts->force_rescue) ? 1 : 0;
+  prm.indices = indices;
+  prm.row_stats = opts ? opts->row_stats : nullptr;
+  prm.ws = ws;
+  for (int64_t r0 = 0; r0 < num_rows; r0 += pl.rows_per_launch) {
+    const int64_t nr = (num_rows - r0) < pl.rows_per_launch ? (num_rows - r0) : pl.rows_per_launch;
+    prm.row_begin = (int32_t)r0;
+    prm.rows = (int32_t)nr;
+    int64_t grid;
+    if (pl.G == 1) {
+      prm.xcd_group = 0;
+      grid = nr;
+    } else {
+      prm.xcd_group = (pl.xcd_group && nr >= 8) ? 1 : 0;
+      grid = prm.xcd_group ? ((nr + 7) / 8) * 8 * pl.G : nr * pl.G;
+    }
+    void* args[] = {&prm};
+    if (hipLaunchKernel(kern, dim3((unsigned)grid), dim3(kBlock), args, 0, stream) != hipSuccess)
+      return TOPK_ELAUNCH;
+  }
+  if (hipGetLastError() != hipSuccess) return TOPK_ELAUNCH;
+  return TOPK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int topk_decode(const float* logits, int64_t row_stride, const int32_t* n_valid, int32_t num_rows,
+                int32_t k, int32_t* indices, void* workspace, size_t workspace_bytes,
+                hipStream_t stream) {
+  return run(0, logits, row_stride, n_valid, nullptr, num_rows, k, indices, 0, workspace,
+             workspace_bytes, stream, nullptr);
+}
+
+int topk_prefill(const float* logits, int64_t row_stride, const int32_t* row_starts,
+                 const int32_t* row_ends, int32_t num_rows, int32_t k, int32_t* indices,
+                 int64_t max_row_len, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return run(1, logits, row_stride, row_starts, row_ends, num_rows, k, indices, max_row_len,
+             workspace, workspace_bytes, stream, nullptr);
+}
+
+int topk_decode_ex(const float* logits, int64_t row_stride, const int32_t* n_valid,
+                   int32_t num_rows, int32_t k, int32_t* indices, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream, const topk_options* opts) {
+  return run(0, logits, row_stride, n_valid, nullptr, num_rows, k, indices, 0, workspace,
+             workspace_bytes, stream, opts);
+}
+
+int topk_prefill_ex(const float* logits, int64_t row_stride, const int32_t* row_starts,
+                    const int32_t* row_ends, int32_t num_rows, int32_t k, int32_t* indices,
+                    int64_t max_row_len, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream, const topk_options* opts) {
+  return run(1, logits, row_stride, row_starts, row_ends, num_rows, k, indices, max_row_len,
+             workspace, workspace_bytes, stream, opts);
+}
+
+size_t topk_workspace_bytes(int32_t num_rows, int64_t max_row_len, int32_t k) {
+  if (num_rows < 0 || !k_ok(k) || max_row_len < 1) return 0;
+  if (num_rows == 0) return 0;
+  return ws_bytes_upper(num_rows, max_row_len, k, 0);
+}
+
+int topk_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!workspace && workspace_bytes) return TOPK_EINVAL;
+  if (!workspace_bytes) return TOPK_OK;
+  return hipMemsetAsync(workspace, 0, workspace_bytes, stream) == hipSuccess ? TOPK_OK
+                                                                              : TOPK_ELAUNCH;
+}
+
+const char* topk_strerror(int status) {
+  switch (status) {
+    case TOPK_OK: return "ok";
+    case TOPK_EINVAL: return "invalid argument (null pointer, num_rows < 0, k not in {512,1024,2048}, row_stride < 1, or row too long)";
+    case TOPK_ELAYOUT: return "unsupported layout (logits must be 16-byte aligned with row_stride % 4 == 0; indices/extents 4-byte aligned)";
+    case TOPK_EWORKSPACE: return "workspace smaller than topk_workspace_bytes()";
+    case TOPK_EDEVICE: return "current device is not gfx950";
+    case TOPK_ELAUNCH: return "HIP launch or allocation failed";
+    default: return "unknown status";
+  }
+}
+
+int topk_plan_query(int32_t num_rows, int64_t row_stride, int64_t max_row_len, int32_t k,
+                    int32_t force_wgs_per_row, int32_t cu_count, int32_t wgs_per_cu, int64_t* out) {
+  if (!out || num_rows < 0 || !k_ok(k) || row_stride < 1 || cu_count < 1 || wgs_per_cu < 1)
+    return TOPK_EINVAL;
+  if (max_row_len < 0) return TOPK_EINVAL;
+  const int64_t env = row_stride;
+  Plan pl;
+  int rc = make_plan(num_rows, env, k, force_wgs_per_row, (int64_t)cu_count * wgs_per_cu, &pl);
+  if (rc != TOPK_OK) return rc;
+  out[0] = pl.G;
+  out[1] = pl.qpt;
+  out[2] = pl.rows_per_launch;
+  out[3] = pl.launches;
+  out[4] = (int64_t)pl.ws_bytes;
+  out[5] = pl.cap;
+  return TOPK_OK;
+}
+
+int topk_validate(int32_t mode, const void* logits, int64_t row_stride, const void* extents,
+                  const void* extents2, int32_t num_rows, int32_t k, const void* indices,
+                  const void* workspace, size_t workspace_bytes, int64_t max_row_len) {
+  if (mode != 0 && mode != 1) return TOPK_EINVAL;
+  int rc = validate(mode, logits, row_stride, extents, extents2, num_rows, k, indices, 0);
+  if (rc != TOPK_OK || num_rows == 0) return rc;
+  if (max_row_len < 0) return TOPK_EINVAL;
+  const int64_t env = row_stride;
+  if (workspace) {
+    Plan pl;
+    rc = make_plan(num_rows, env, k, 0, (int64_t)1 << 40, &pl);
+    if (rc != TOPK_OK) return rc;
+    if (pl.G > 1 && workspace_bytes < ws_bytes_upper(num_rows, env, k, 0)) return TOPK_EWORKSPACE;
+  }
+  return TOPK_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,166 @@
+/*
+ * exact_row_top.h -- C ABI of the MI355X (gfx950) exact per-row top-K library.
+ *
+ * The operation is the exact top-K selection a sparse-attention (DSA) indexer
+ * runs over one fp32 score row per query, as stated on the TensorRT-LLM pages:
+ *
+ *  - "Self-sampling GVR V2 prefill indexer top-K" (PR 18702), section
+ *    "Kernel": per row r, the top-K of logits[r, ks:ke] with ks = row_starts[r]
+ *    and ke = row_ends[r], written in the row's LOCAL frame (column - ks) with a
+ *    trailing -1 pad, and the identity 0..nv-1 when nv = ke - ks <= K.
+ *  - "Block-skip fast path for self-sampling GVR top-K decode" (PR 18122),
+ *    first commit message ("Contract"): fp32 scores, K in {512, 1024, 2048},
+ *    exact top-K in which indices may interchange only inside the K-th value's
+ *    tie class; the short-row commit (identity then -1); the varlen commit
+ *    (per-row valid lengths read on the device, no host reads).
+ *
+ * How it is computed (Guess-Verify-Refine, PR 20998 "GVR K=2048 reg_clus with
+ * block64 sampling and parallel rescue", sections "Why the GLM row overflows"
+ * and "What changes"): sample K scores as K/64 blocks of 64 spread over the
+ * row, bracket the K-th value with the sample's min/max, histogram the row
+ * against that bracket, find the bin where the count from the top crosses K,
+ * keep the bins above it, compact the crossing bin's members as candidates and
+ * refine them exactly; an invalid bracket or an oversized crossing bin takes an
+ * exact radix-select rescue over the whole row inside the same launch.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All array arguments are DEVICE pointers owned by the caller; the library
+ *    never frees or retains them.  Calls are stream-ordered on `stream`
+ *    (NULL = the null stream): the host never waits, never reads device data
+ *    and, when `workspace` is given, never allocates.
+ *  - logits: fp32 [num_rows][row_stride], unit inner stride, base 16-byte
+ *    aligned, row_stride a multiple of 4 floats (the float4 row-stride gate of
+ *    PR 18702's format check).  Every row's full stride must be readable: the
+ *    kernel loads whole aligned float4 groups, and masks lanes outside the
+ *    window by position, so values outside [ks, ke) (poison) never reach the
+ *    selection.
+ *  - indices: int32 [num_rows][k], 4-byte aligned.  Long rows (nv > k) get k
+ *    distinct positions in [0, nv) in unspecified order; short rows get
+ *    0..nv-1 then -1.
+ *  - NaN inside a window is outside the contract (PR 18122, varlen commit:
+ *    "NaN-ordering limitation"): the kernel stays memory-safe and still writes
+ *    k distinct in-window indices, but which ones is unspecified.  +-inf are
+ *    ordinary values; -0 and +0 are equal.
+ *  - workspace: optional caller-owned device buffer of at least
+ *    topk_workspace_bytes(...) bytes, zeroed ONCE by topk_workspace_init before
+ *    its first use; every call returns it to that resting state (histograms,
+ *    cursors and counters back to zero; only a per-row barrier generation word
+ *    keeps counting), so a captured graph can replay without a memset.  The
+ *    split tier's row barriers need the workgroups of a launch to be resident
+ *    together; the plan bounds each launch by the device's resident capacity,
+ *    so kernels that pin the GPU's compute units for their whole lifetime must
+ *    not run beside these calls.  Calls that run concurrently (different
+ *    streams) must not share one workspace.  NULL selects a per-device slab
+ *    the library allocates on first need, keeps until process exit, and grows
+ *    only when a larger plan needs it (allocation is not capture-safe).
+ *  - Return value: TOPK_OK or one of the TOPK_E* codes below; nothing else
+ *    crosses the ABI (no exceptions).  Argument errors are detected on the
+ *    host before anything is launched.
+ */
+#ifndef EXACT_ROW_TOP_H_
+#define EXACT_ROW_TOP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  TOPK_OK = 0,
+  TOPK_EINVAL = 1,     /* null pointer with num_rows > 0, num_rows < 0, k not in
+                          {512,1024,2048}, row_stride < 1, bad option value */
+  TOPK_ELAYOUT = 2,    /* logits not 16-byte aligned, row_stride % 4 != 0,
+                          indices / extents not 4-byte aligned */
+  TOPK_EWORKSPACE = 3, /* caller workspace smaller than topk_workspace_bytes */
+  TOPK_EDEVICE = 4,    /* current device is not gfx950, or no device */
+  TOPK_ELAUNCH = 5,    /* a HIP launch or allocation failed */
+};
+
+/* Decode form (PR 18122 varlen contract with next_n = 1, compress ratio 1):
+ * row r selects from logits[r, 0:nv) with nv = clamp(n_valid[r], 0,
+ * row_stride).  n_valid: device int32[num_rows]. */
+int topk_decode(const float* logits, int64_t row_stride, const int32_t* n_valid,
+                int32_t num_rows, int32_t k, int32_t* indices, void* workspace,
+                size_t workspace_bytes, hipStream_t stream);
+
+/* Prefill form (PR 18702 "Kernel"): row r selects from logits[r, ks:ke) with
+ * ks = clamp(row_starts[r], 0, row_stride), ke = clamp(row_ends[r], ks,
+ * row_stride); indices are ks-relative.  row_starts / row_ends: device
+ * int32[num_rows].  max_row_len: advisory host-side bound on ke - ks (0 =
+ * none, < 0 rejected).  Launch shapes are always sized for row_stride, so any
+ * window inside the stride is handled whatever the hint says. */
+int topk_prefill(const float* logits, int64_t row_stride, const int32_t* row_starts,
+                 const int32_t* row_ends, int32_t num_rows, int32_t k, int32_t* indices,
+                 int64_t max_row_len, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream);
+
+/* Bytes of workspace a call with num_rows rows of stride `max_row_len` needs
+ * (pass the row_stride of the call; 0 when the plan uses one workgroup per
+ * row and needs none).  The value does not depend on the device.  Returns 0
+ * for invalid arguments as well. */
+size_t topk_workspace_bytes(int32_t num_rows, int64_t max_row_len, int32_t k);
+
+/* Zero a workspace once before its first use (stream-ordered memset). */
+int topk_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Static text for a status code. */
+const char* topk_strerror(int status);
+
+/* ---- Test and diagnostic surface ------------------------------------------
+ * Same operations with knobs for tests.  `opts` may be NULL (= defaults).
+ *  force_wgs_per_row: 0 = automatic plan; 1 = one workgroup per row; G > 1 =
+ *      G workgroups per row (G <= 64), subject to the plan still fitting.
+ *  force_rescue: nonzero = treat every long row's bracket as invalid, so the
+ *      exact radix rescue runs on every long row.
+ *  row_stats: optional device int32[num_rows][TOPK_STATS_WORDS]; per row:
+ *      [0] path (0 short, 1 bracket + refine, 2 rescue: invalid bracket,
+ *          3 rescue: crossing bin over the candidate cap),
+ *      [1] m (crossing-bin population, -1 if no histogram ran),
+ *      [2] above (count in bins above the crossing bin, -1 if none),
+ *      [3] crossing bin index (-1 if none),
+ *      [4] bit pattern of the sample minimum, [5] of the sample maximum,
+ *      [6] workgroups per row, [7] candidate cap.
+ */
+#define TOPK_STATS_WORDS 8
+
+typedef struct topk_options {
+  int32_t force_wgs_per_row;
+  int32_t force_rescue;
+  int32_t* row_stats;
+} topk_options;
+
+int topk_decode_ex(const float* logits, int64_t row_stride, const int32_t* n_valid,
+                   int32_t num_rows, int32_t k, int32_t* indices, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream, const topk_options* opts);
+
+int topk_prefill_ex(const float* logits, int64_t row_stride, const int32_t* row_starts,
+                    const int32_t* row_ends, int32_t num_rows, int32_t k, int32_t* indices,
+                    int64_t max_row_len, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream, const topk_options* opts);
+
+/* Host-only planning and validation, callable without a GPU.  Fills
+ * out[0..5] = {workgroups per row, quads per thread, rows per launch,
+ * launches, workspace bytes, candidate cap} for the shapes given (the same
+ * plan topk_decode / topk_prefill would use; `force_wgs_per_row` as in
+ * topk_options; `cu_count` and `wgs_per_cu` stand in for the device's resident
+ * capacity).  Returns a status code. */
+int topk_plan_query(int32_t num_rows, int64_t row_stride, int64_t max_row_len, int32_t k,
+                    int32_t force_wgs_per_row, int32_t cu_count, int32_t wgs_per_cu,
+                    int64_t* out);
+
+/* Host-side argument validation exactly as the entry points run it (no device
+ * access).  mode: 0 decode (extents = n_valid, extents2 unused), 1 prefill. */
+int topk_validate(int32_t mode, const void* logits, int64_t row_stride, const void* extents,
+                  const void* extents2, int32_t num_rows, int32_t k, const void* indices,
+                  const void* workspace, size_t workspace_bytes, int64_t max_row_len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_ROW_TOP_H_ */

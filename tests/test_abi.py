@@ -1,0 +1,131 @@
+"""Host-side tests of the C-ABI library (no GPU, no compute calls).
+
+- the shared library loads and exports every function include/exact_row_top.h
+  declares;
+- argument validation returns the documented status codes without touching a
+  device;
+- launch planning picks the tiers the design states for the five workloads.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "exact_row_top.h")
+
+ert = pytest.importorskip("exact_row_top_amd")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(topk_\w+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for required in ("topk_decode", "topk_prefill", "topk_workspace_bytes",
+                     "topk_workspace_init", "topk_strerror"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ert.load_library()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_strerror_covers_codes():
+    for code in range(6):
+        assert ert.strerror(code)
+    assert "unknown" in ert.strerror(99)
+
+
+P16 = 1 << 20  # a fake, 16-byte aligned "device" address (never dereferenced)
+
+
+def _validate(mode=0, logits=P16, stride=4096, e1=P16, e2=P16, rows=4, k=512, idx=P16,
+              ws=None, ws_bytes=0, max_len=0):
+    return ert.load_library().topk_validate(mode, logits, stride, e1, e2, rows, k, idx, ws,
+                                            ws_bytes, max_len)
+
+
+def test_validate_ok():
+    assert _validate() == 0
+    assert _validate(mode=1) == 0
+    assert _validate(rows=0, logits=None, e1=None, e2=None, idx=None) == 0  # empty is a no-op
+
+
+@pytest.mark.parametrize("k", [0, 1, 256, 511, 513, 2047, 4096, -512])
+def test_validate_rejects_k(k):
+    assert _validate(k=k) == ert.TOPK_EINVAL
+
+
+def test_validate_rejects_nulls_and_counts():
+    assert _validate(rows=-1) == ert.TOPK_EINVAL
+    assert _validate(logits=None) == ert.TOPK_EINVAL
+    assert _validate(e1=None) == ert.TOPK_EINVAL
+    assert _validate(idx=None) == ert.TOPK_EINVAL
+    assert _validate(mode=1, e2=None) == ert.TOPK_EINVAL
+    assert _validate(mode=0, e2=None) == 0  # decode has no second extent
+    assert _validate(stride=0) == ert.TOPK_EINVAL
+    assert _validate(mode=2) == ert.TOPK_EINVAL
+    assert _validate(max_len=-1) == ert.TOPK_EINVAL
+
+
+def test_validate_layout():
+    assert _validate(logits=P16 + 4) == ert.TOPK_ELAYOUT  # float aligned, not float4 aligned
+    assert _validate(logits=P16 + 8) == ert.TOPK_ELAYOUT
+    assert _validate(stride=4098) == ert.TOPK_ELAYOUT
+    assert _validate(stride=4099) == ert.TOPK_ELAYOUT
+    assert _validate(idx=P16 + 2) == ert.TOPK_ELAYOUT
+    assert _validate(e1=P16 + 1) == ert.TOPK_ELAYOUT
+    assert _validate(mode=1, e2=P16 + 3) == ert.TOPK_ELAYOUT
+
+
+def test_validate_workspace_size():
+    need = ert.workspace_bytes(64, 131072, 2048)
+    assert need > 0
+    assert _validate(stride=131072, rows=64, k=2048, ws=P16, ws_bytes=need) == 0
+    assert _validate(stride=131072, rows=64, k=2048, ws=P16, ws_bytes=need - 1) == ert.TOPK_EWORKSPACE
+
+
+def test_workspace_bytes():
+    assert ert.workspace_bytes(4096, 16640, 1024) == 0      # one workgroup per row
+    assert ert.workspace_bytes(0, 4096, 512) == 0
+    assert ert.workspace_bytes(4, 4096, 513) == 0             # invalid k
+    a = ert.workspace_bytes(8, 262144, 2048)
+    b = ert.workspace_bytes(64, 131072, 2048)
+    assert 0 < a < b
+
+
+def test_plans_for_the_workloads():
+    # many short-to-mid rows: one workgroup per row, whole window resident
+    p = ert.plan_query(4096, 16640, 1024)
+    assert p["wgs_per_row"] == 1 and p["quads_per_thread"] * 256 * 4 >= 16640 + 6
+    # few long rows: split, the row's parts cover the whole stride
+    for rows, stride, k in ((64, 131072, 2048), (1, 131072, 512), (8, 131072, 512),
+                            (8, 262144, 2048)):
+        p = ert.plan_query(rows, stride, k)
+        assert p["wgs_per_row"] > 1
+        assert p["wgs_per_row"] * p["quads_per_thread"] * 256 >= (stride + 6) // 4
+        assert p["cap"] == min(p["wgs_per_row"] * 4096, 32 * k, 16384)
+    # capacity bounds rows per launch (co-resident split workgroups)
+    p = ert.plan_query(64, 131072, 2048, cu_count=16, wgs_per_cu=2)
+    assert p["rows_per_launch"] * p["wgs_per_row"] <= 32 and p["launches"] > 1
+
+
+def test_plan_forced_tiers():
+    p = ert.plan_query(8, 16384, 512, force_wgs_per_row=1)
+    assert p["wgs_per_row"] == 1
+    p = ert.plan_query(8, 16384, 512, force_wgs_per_row=4)
+    assert p["wgs_per_row"] == 4
+    with pytest.raises(ert.TopKError):
+        ert.plan_query(8, 131072, 512, force_wgs_per_row=1)   # row does not fit one workgroup
+    with pytest.raises(ert.TopKError):
+        ert.plan_query(8, 4096, 512, force_wgs_per_row=65)
+    with pytest.raises(ert.TopKError):
+        ert.plan_query(1, 64 * 17 * 256 * 4 + 64, 512)        # longer than the largest plan
