@@ -35,7 +35,16 @@ constexpr int kMaxWgsPerRow = 64;
 constexpr int kMaxSlots = 256;  // split rows per launch (workspace slots)
 constexpr int kStatsWords = 8;
 
-// Workspace layout: a 256-byte header, then kMaxSlots-bounded slots.
+// Workspace layout (bytes):
+//   [0, 256)                          error flags (word 0)
+//   [256, 256 + kMaxSlots * 256)      one SlotHeader per split row of a launch
+//   then, per slot, a data block of slot_data_bytes(G):
+//     candidate keys [kSplitCapMax] | candidate indices [kSplitCapMax] |
+//     per-workgroup histograms [G][kBins] | per-workgroup digit counts [G][4][256]
+// Only the headers hold state between calls, and the last workgroup of a row
+// returns its header to zero; their place does not depend on the plan, so
+// one workspace serves any plan it is large enough for.  Data blocks are
+// written densely before they are read and need no clearing.
 struct SlotHeader {
   uint32_t bar_count;  // barrier arrivals (returns to 0 after each barrier)
   uint32_t bar_gen;    // barrier generation (monotone, never reset)
@@ -47,12 +56,18 @@ struct SlotHeader {
 };
 static_assert(sizeof(SlotHeader) == 256, "slot header size");
 
-constexpr size_t kWsHeaderBytes = 256;  // word 0: error flags
-constexpr size_t kSlotHistOff = sizeof(SlotHeader);
-constexpr size_t kSlotDigitOff = kSlotHistOff + sizeof(uint32_t) * kBins;
-constexpr size_t kSlotKeyOff = kSlotDigitOff + sizeof(uint32_t) * 4 * 256;
+constexpr size_t kWsHeaderBytes = 256;
+constexpr size_t kWsSlotHeadersBytes = sizeof(SlotHeader) * kMaxSlots;
+constexpr size_t kWsDataOff = kWsHeaderBytes + kWsSlotHeadersBytes;
+constexpr size_t kSlotKeyOff = 0;
 constexpr size_t kSlotIdxOff = kSlotKeyOff + sizeof(uint32_t) * kSplitCapMax;
-constexpr size_t kSlotBytes = kSlotIdxOff + sizeof(int32_t) * kSplitCapMax;
+constexpr size_t kSlotWgHistOff = kSlotIdxOff + sizeof(int32_t) * kSplitCapMax;
+constexpr size_t slot_data_bytes(int wgs_per_row) {
+  return kSlotWgHistOff + sizeof(uint32_t) * ((size_t)kBins + 4 * 256) * (size_t)wgs_per_row;
+}
+constexpr size_t ws_bytes_for(int slots, int wgs_per_row) {
+  return kWsDataOff + (size_t)slots * slot_data_bytes(wgs_per_row);
+}
 
 // Error flags written by the kernel into workspace word 0.
 constexpr uint32_t kErrBarrierTimeout = 1u;
@@ -72,6 +87,7 @@ struct GvrParams {
   int32_t* indices;
   int32_t* row_stats;  // optional
   unsigned char* ws;   // workspace base (split tier), or nullptr
+  size_t slot_data_bytes;  // bytes per split-row data block
 };
 
 }  // namespace ert

@@ -89,7 +89,7 @@ int make_plan(int32_t num_rows, int64_t env_len, int32_t k, int32_t force_g, int
     const int64_t slots = p.xcd_group ? ((rpl + 7) / 8) * 8 : rpl;
     if (p.xcd_group && slots * G > capacity) p.xcd_group = 0;
     const int64_t nslots = p.xcd_group ? slots : rpl;
-    p.ws_bytes = kWsHeaderBytes + (size_t)nslots * kSlotBytes;
+    p.ws_bytes = ws_bytes_for((int)nslots, G);
     int64_t cap = (int64_t)G * kSplitCapPerWg;
     if (cap > 32LL * k) cap = 32LL * k;
     if (cap > kSplitCapMax) cap = kSplitCapMax;
@@ -107,7 +107,7 @@ size_t ws_bytes_upper(int32_t num_rows, int64_t env_len, int32_t k, int32_t forc
   if (p.G == 1) return 0;
   int64_t rpl = num_rows < kMaxSlots ? num_rows : kMaxSlots;
   int64_t slots = ((rpl + 7) / 8) * 8;
-  return kWsHeaderBytes + (size_t)slots * kSlotBytes;
+  return ws_bytes_for((int)slots, p.G);
 }
 
 int validate(int mode, const void* logits, int64_t row_stride, const void* e1, const void* e2,
@@ -233,6 +233,7 @@ int run(int mode, const float* logits, int64_t row_stride, const int32_t* e1, co
   prm.indices = indices;
   prm.row_stats = opts ? opts->row_stats : nullptr;
   prm.ws = ws;
+  prm.slot_data_bytes = slot_data_bytes(pl.G);
   for (int64_t r0 = 0; r0 < num_rows; r0 += pl.rows_per_launch) {
     const int64_t nr = (num_rows - r0) < pl.rows_per_launch ? (num_rows - r0) : pl.rows_per_launch;
     prm.row_begin = (int32_t)r0;
