@@ -63,6 +63,8 @@ def load_library():
     lib.topk_strerror.restype = ctypes.c_char_p
     lib.topk_plan_query.argtypes = [I32, I64, I64, I32, I32, I32, I32, ctypes.POINTER(I64)]
     lib.topk_plan_query.restype = ctypes.c_int
+    lib.topk_device_query.argtypes = [ctypes.POINTER(I64)]
+    lib.topk_device_query.restype = ctypes.c_int
     lib.topk_validate.argtypes = [I32, P, I64, P, P, I32, I32, P, P, SZ, I64]
     lib.topk_validate.restype = ctypes.c_int
     _lib = lib
@@ -85,20 +87,34 @@ def workspace_bytes(num_rows: int, row_stride: int, k: int) -> int:
 def plan_query(num_rows: int, row_stride: int, k: int, force_wgs_per_row: int = 0,
                cu_count: int = 256, wgs_per_cu: int = 2) -> dict:
     """The launch plan the library would use (host-only, no GPU needed)."""
-    out = (ctypes.c_int64 * 6)()
+    out = (ctypes.c_int64 * 7)()
     _check(load_library().topk_plan_query(num_rows, row_stride, 0, k, force_wgs_per_row,
                                           cu_count, wgs_per_cu, out))
-    keys = ("wgs_per_row", "quads_per_thread", "rows_per_launch", "launches", "workspace_bytes", "cap")
+    keys = ("wgs_per_row", "quads_per_thread", "rows_per_launch", "launches", "workspace_bytes",
+            "cap", "block")
     return dict(zip(keys, (int(x) for x in out)))
+
+
+def device_query() -> dict:
+    """Compute units and split-tier residency the planner sees (needs a GPU)."""
+    out = (ctypes.c_int64 * 37)()
+    _check(load_library().topk_device_query(out))
+    def tab(off):
+        return {k: [int(out[off + 3 * ki + qi]) for qi in range(3)] for ki, k in enumerate(VALID_K)}
+    return {"cus": int(out[0]), "split_wgs_per_cu": tab(1), "runtime_wgs_per_cu": tab(10),
+            "vgprs": tab(19), "lds_bytes": tab(28)}
 
 
 # ---------------------------------------------------------------------------
 # torch marshalling
 # ---------------------------------------------------------------------------
 
-def _stream_ptr(stream) -> Optional[int]:
+def _stream_ptr(stream, device) -> Optional[int]:
     import torch
     if stream is None:
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        if raw is not None:
+            return int(raw(device.index if device.index is not None else torch.cuda.current_device())) or None
         stream = torch.cuda.current_stream()
     return int(stream.cuda_stream) or None
 
@@ -120,14 +136,16 @@ def _logits_layout(logits):
     _require(logits, "logits", torch.float32, 2)
     if logits.stride(1) != 1:
         raise ValueError("logits must have unit inner stride")
-    rows = logits.shape[0]
-    row_stride = logits.stride(0) if rows > 1 else logits.shape[1]
-    if rows > 1 and row_stride < logits.shape[1]:
+    rows, width = logits.shape
+    row_stride = logits.stride(0) if rows > 1 else width
+    if rows > 1 and row_stride < width:
         raise ValueError("logits rows overlap")
-    # the kernel may read any aligned float4 of a row's full stride
-    need = (logits.storage_offset() + rows * row_stride) * 4
-    if rows and logits.untyped_storage().nbytes() < need:
-        raise ValueError("logits storage must hold rows x row_stride floats (full last row)")
+    if row_stride != width:
+        # a column-sliced view: the kernel may read any aligned float4 of a
+        # row's full stride, so the storage must hold the whole last row
+        need = (logits.storage_offset() + rows * row_stride) * 4
+        if rows and logits.untyped_storage().nbytes() < need:
+            raise ValueError("logits storage must hold rows x row_stride floats (full last row)")
     return rows, int(row_stride)
 
 
@@ -172,7 +190,7 @@ def topk_decode(logits, n_valid, k: int, indices=None, *, workspace=None, stream
     out = _out(indices, rows, k, logits.device)
     wp, wb = _ws(workspace)
     opts = _opts(force_wgs_per_row, force_rescue, row_stats, rows)
-    s = _stream_ptr(stream)
+    s = _stream_ptr(stream, logits.device)
     if opts is None:
         rc = lib.topk_decode(logits.data_ptr(), row_stride, n_valid.data_ptr(), rows, k,
                              out.data_ptr(), wp, wb, s)
@@ -197,7 +215,7 @@ def topk_prefill(logits, row_starts, row_ends, k: int, indices=None, *, max_row_
     out = _out(indices, rows, k, logits.device)
     wp, wb = _ws(workspace)
     opts = _opts(force_wgs_per_row, force_rescue, row_stats, rows)
-    s = _stream_ptr(stream)
+    s = _stream_ptr(stream, logits.device)
     if opts is None:
         rc = lib.topk_prefill(logits.data_ptr(), row_stride, row_starts.data_ptr(),
                               row_ends.data_ptr(), rows, k, out.data_ptr(), int(max_row_len),
@@ -217,7 +235,7 @@ def new_workspace(num_rows: int, row_stride: int, k: int, device="cuda", stream=
     if nbytes == 0:
         return None
     ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
-    _check(load_library().topk_workspace_init(ws.data_ptr(), nbytes, _stream_ptr(stream)))
+    _check(load_library().topk_workspace_init(ws.data_ptr(), nbytes, _stream_ptr(stream, ws.device)))
     return ws
 
 

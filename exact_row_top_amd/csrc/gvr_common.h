@@ -8,17 +8,13 @@
 
 namespace ert {
 
-// Workgroup: four wave64s.
-constexpr int kBlock = 256;
-constexpr int kWaves = kBlock / 64;
-
 // Value-histogram bins over the sampled bracket.  The pages do not state a bin
 // count; 2048 keeps the crossing bin of a Gaussian-like row at tens of members
 // for every K while the LDS histogram stays at 8 KiB.
 constexpr int kBins = 2048;
 
-// Candidate capacity of the one-workgroup tier (LDS, shares storage with the
-// histogram once the crossing bin is known).
+// Candidate capacity held in LDS (one-workgroup tier, and the split tier's
+// final refine).
 constexpr int kSingleCap = 2048;
 
 // Per-row candidate storage of the split tier (workspace).  The pages' rescue
@@ -27,24 +23,36 @@ constexpr int kSingleCap = 2048;
 constexpr int kSplitCapMax = 16384;
 constexpr int kSplitCapPerWg = 4096;
 
-// Quads (float4 groups) per thread the kernels are instantiated for.
-constexpr int kQptList[] = {4, 8, 17};
-constexpr int kQptMax = 17;
+// Split tier: a row whose sampled count above the floor bin predicts more
+// than this many scores there goes straight to the parallel rescue.
+constexpr int kPredictMax = kSplitCapMax / 2;
+
+// Launch variants: (workgroup size, float4 groups per thread).
+struct Variant {
+  int block;
+  int qpt;
+};
+// One workgroup per row; resident capacity block * qpt * 4 scores.
+constexpr Variant kSingleVariants[] = {{256, 8}, {512, 9}, {1024, 9}};
+// G workgroups per row, each holding 1/G of the row.
+constexpr int kSplitBlock = 256;
+constexpr int kSplitQpt[] = {4, 8, 17};
 
 constexpr int kMaxWgsPerRow = 64;
 constexpr int kMaxSlots = 256;  // split rows per launch (workspace slots)
 constexpr int kStatsWords = 8;
 
 // Workspace layout (bytes):
-//   [0, 256)                          error flags (word 0)
-//   [256, 256 + kMaxSlots * 256)      one SlotHeader per split row of a launch
-//   then, per slot, a data block of slot_data_bytes(G):
-//     candidate keys [kSplitCapMax] | candidate indices [kSplitCapMax] |
-//     per-workgroup histograms [G][kBins] | per-workgroup digit counts [G][4][256]
-// Only the headers hold state between calls, and the last workgroup of a row
-// returns its header to zero; their place does not depend on the plan, so
-// one workspace serves any plan it is large enough for.  Data blocks are
-// written densely before they are read and need no clearing.
+//   [0, 256)                             error flags (word 0)
+//   kMaxSlots fixed blocks of 4352 bytes: SlotHeader + digit counts [4][256]
+//   then one data block per slot: candidate (key, index) pairs
+//   [kSplitCapMax]; consecutive blocks are skewed by 4 KiB so the slots'
+//   first bytes do not all land on the same memory channels
+// The fixed blocks hold every word that carries state between calls, and the
+// last workgroup of a row returns them to zero (only the barrier generation
+// keeps counting); their place does not depend on the plan, so one workspace
+// serves any plan it is large enough for.  Data blocks are written before they
+// are read and need no clearing.
 struct SlotHeader {
   uint32_t bar_count;  // barrier arrivals (returns to 0 after each barrier)
   uint32_t bar_gen;    // barrier generation (monotone, never reset)
@@ -56,18 +64,16 @@ struct SlotHeader {
 };
 static_assert(sizeof(SlotHeader) == 256, "slot header size");
 
+struct SlotFixed {
+  SlotHeader hdr;
+  uint32_t dig[4][256];  // rescue digit counts, one row per radix level
+};
+static_assert(sizeof(SlotFixed) == 4352, "slot fixed block size");
+
 constexpr size_t kWsHeaderBytes = 256;
-constexpr size_t kWsSlotHeadersBytes = sizeof(SlotHeader) * kMaxSlots;
-constexpr size_t kWsDataOff = kWsHeaderBytes + kWsSlotHeadersBytes;
-constexpr size_t kSlotKeyOff = 0;
-constexpr size_t kSlotIdxOff = kSlotKeyOff + sizeof(uint32_t) * kSplitCapMax;
-constexpr size_t kSlotWgHistOff = kSlotIdxOff + sizeof(int32_t) * kSplitCapMax;
-constexpr size_t slot_data_bytes(int wgs_per_row) {
-  return kSlotWgHistOff + sizeof(uint32_t) * ((size_t)kBins + 4 * 256) * (size_t)wgs_per_row;
-}
-constexpr size_t ws_bytes_for(int slots, int wgs_per_row) {
-  return kWsDataOff + (size_t)slots * slot_data_bytes(wgs_per_row);
-}
+constexpr size_t kWsDataOff = kWsHeaderBytes + sizeof(SlotFixed) * kMaxSlots;
+constexpr size_t kSlotDataBytes = 2 * sizeof(uint32_t) * kSplitCapMax + 4096;
+constexpr size_t ws_bytes_for(int slots) { return kWsDataOff + (size_t)slots * kSlotDataBytes; }
 
 // Error flags written by the kernel into workspace word 0.
 constexpr uint32_t kErrBarrierTimeout = 1u;
@@ -87,7 +93,6 @@ struct GvrParams {
   int32_t* indices;
   int32_t* row_stats;  // optional
   unsigned char* ws;   // workspace base (split tier), or nullptr
-  size_t slot_data_bytes;  // bytes per split-row data block
 };
 
 }  // namespace ert

@@ -1,17 +1,6 @@
 // gvr_kernels.hip -- gfx950 kernels of the exact per-row top-K
 // (Guess-Verify-Refine with block64 sampling and an exact radix rescue).
 //
-// One fused kernel template serves both tiers:
-//  * one workgroup per row (SPLIT = false): the row is resident in the
-//    workgroup's VGPRs, every merge happens in LDS, nothing is shared across
-//    workgroups;
-//  * G workgroups per row (SPLIT = true): each workgroup keeps 1/G of the row
-//    resident in VGPRs.  Histograms merge through a per-row workspace slot
-//    (dense per-workgroup slices, summed by every workgroup after a
-//    generation barrier), candidates are appended to the slot, and the last
-//    workgroup to finish refines them and clears the slot's counters so the
-//    next call (or graph replay) finds them at rest.
-//
 // Steps per long row (nv > K), following the TensorRT-LLM page "GVR K=2048
 // reg_clus with block64 sampling and parallel rescue" (PR 20998), sections
 // "Why the GLM row overflows" and "What changes":
@@ -26,11 +15,29 @@
 //  4. the crossing bin b*: the highest bin whose count from the top reaches K;
 //     everything above it is selected, b* holds m candidates of which
 //     need = K - above are selected;
-//  5. compact winners straight to the output and candidates to a buffer;
+//  5. compact winners to the output and candidates to a buffer;
 //  6. refine: the `need` largest candidates, exactly;
-//  7. rescue when the bracket is invalid or m exceeds the candidate cap: an
-//     exact 4 x 8-bit radix select over the whole row's resident keys, using
-//     every workgroup of the row, inside the same launch.
+//  7. rescue when the bracket is invalid or the candidates overflow: an exact
+//     4 x 8-bit radix select over the whole row's resident keys, using every
+//     workgroup of the row, inside the same launch.
+//
+// Two tiers share the steps:
+//  * one workgroup per row (SPLIT = false): the whole window is resident in
+//    the workgroup's VGPRs, histogram, crossing bin, compaction and refine all
+//    run in LDS, nothing is shared with other workgroups;
+//  * G workgroups per row (SPLIT = true): each keeps 1/G of the row resident.
+//    Every workgroup derives the same bracket and, from the sample's own
+//    histogram, the same floor bin b_lo below which the crossing bin (almost
+//    surely) is not; it appends its scores in bins >= b_lo to the row's
+//    candidate list with one atomic and counts itself done.  The last
+//    workgroup histograms that list -- the row's histogram restricted to
+//    bins >= b_lo, so the crossing bin, `above` and m are exactly those of
+//    the full histogram -- and selects.  No workgroup waits for another on
+//    this path.  Rows whose sample predicts a crowded top (tie-heavy rows)
+//    and rows with an invalid bracket take the parallel rescue, whose radix
+//    levels merge through the workspace with a generation barrier.  A row the
+//    prediction missed (the list overflows, or holds fewer than K) is
+//    finished by the last workgroup alone from the row in memory.
 //
 // Ordering: scores compare as IEEE values with -0 == +0; the order-preserving
 // key maps a float to a uint32 whose unsigned order is that value order.
@@ -87,9 +94,79 @@ __device__ __forceinline__ uint32_t load_agent(const uint32_t* p) {
 __device__ __forceinline__ void lds_inc(uint32_t* p) {
   __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
+__device__ __forceinline__ uint32_t lds_take(uint32_t* p) {
+  return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Count one per active lane into h[d]; when every active lane of the wave
+// has the same d (tie-heavy rows), one lane adds them all at once instead of
+// 64 conflicting increments.  Must be reached by the whole wave.
+__device__ __forceinline__ void lds_inc_agg(uint32_t* h, uint32_t d, bool act) {
+  const uint64_t am = __ballot(act);
+  if (am == 0ull) return;
+  const int fl = __ffsll((unsigned long long)am) - 1;
+  const uint32_t d0 = __shfl(d, fl, 64);
+  const uint64_t same = __ballot(act && d == d0);
+  if (same == am) {
+    if (lane_id() == fl)
+      __hip_atomic_fetch_add(&h[d0], (uint32_t)__popcll(am), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_WORKGROUP);
+  } else if (act) {
+    __hip_atomic_fetch_add(&h[d], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+}
+
+// Append the lanes with `pred` to an LDS-counted list: one atomic per wave,
+// lane order inside the wave.  Returns each predicated lane's position.
+// Must be reached by the whole wave.
+__device__ __forceinline__ uint32_t wave_append(bool pred, uint32_t* ctr) {
+  const uint64_t m = __ballot(pred);
+  uint32_t base = 0;
+  if (m != 0ull) {
+    const int leader = __ffsll((unsigned long long)m) - 1;
+    if (lane_id() == leader)
+      base = __hip_atomic_fetch_add(ctr, (uint32_t)__popcll(m), __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_WORKGROUP);
+    base = __shfl(base, leader, 64);
+  }
+  const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+  return base + below;
+}
+
+// Rank-count selection of the `need` largest among m <= kRankMax candidates
+// held in LDS (key[], idx[]): a candidate's rank is the number with a larger
+// key, or an equal key and a smaller index; ranks below `need` go to
+// out[base + rank] (value descending, smallest index first inside a tie).
+// The arrays are padded to a multiple of 4 with keys that rank nothing.
+template <int BLOCK>
+__device__ __forceinline__ void rank_select(uint32_t* key, int32_t* idx, uint32_t m, uint32_t need,
+                                            int32_t* out, uint32_t base) {
+  const int t = threadIdx.x;
+  const uint32_t m4 = (m + 3u) & ~3u;
+  if ((uint32_t)t >= m && (uint32_t)t < m4) {
+    key[t] = 0u;
+    idx[t] = 0x7FFFFFFF;
+  }
+  __syncthreads();
+  if ((uint32_t)t < m) {
+    const uint32_t kk = key[t];
+    const int32_t ii = idx[t];
+    uint32_t rank = 0;
+    for (uint32_t j = 0; j < m4; j += 4) {
+      const uint4 kj = *reinterpret_cast<const uint4*>(key + j);
+      const int4 ij = *reinterpret_cast<const int4*>(idx + j);
+      rank += (kj.x > kk || (kj.x == kk && ij.x < ii)) ? 1u : 0u;
+      rank += (kj.y > kk || (kj.y == kk && ij.y < ii)) ? 1u : 0u;
+      rank += (kj.z > kk || (kj.z == kk && ij.z < ii)) ? 1u : 0u;
+      rank += (kj.w > kk || (kj.w == kk && ij.w < ii)) ? 1u : 0u;
+    }
+    if (rank < need) out[base + rank] = ii;
+  }
+}
 
 // ---------------------------------------------------------------------------
-// Wave and block primitives (kBlock threads = kWaves wave64s)
+// Wave and block primitives
 // ---------------------------------------------------------------------------
 
 template <int CTRL>
@@ -122,7 +199,8 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
   return v;
 }
 
-// Min and max over a wave (result in every lane, read from lane 63).
+// Min and max over a wave (result in every lane, read from lane 63).  NaN
+// inputs are ignored by fminf / fmaxf.
 __device__ __forceinline__ void wave_minmax(float& mn, float& mx) {
   const int l = lane_id();
   const int rl = l & 15;
@@ -146,15 +224,17 @@ __device__ __forceinline__ void wave_minmax(float& mn, float& mx) {
 }
 
 // Exclusive prefix sum over the block in thread order; `total` gets the sum.
-// `sm` holds kWaves words.  Contains two __syncthreads.
+// `sm` holds BLOCK/64 words.  Contains two __syncthreads.
+template <int BLOCK>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sm, uint32_t& total) {
+  constexpr int W = BLOCK / 64;
   const uint32_t inc = wave_incl_scan(v);
   const int w = threadIdx.x >> 6;
   if (lane_id() == 63) sm[w] = inc;
   __syncthreads();
   uint32_t off = 0, tot = 0;
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
+  for (int i = 0; i < W; ++i) {
     const uint32_t s = sm[i];
     off += (i < w) ? s : 0u;
     tot += s;
@@ -172,25 +252,26 @@ struct Cross {
 };
 
 // Find the highest bin b with sum_{b' >= b} h[b'] >= target over NBINS bins,
-// where load(b) returns h[b].  Thread t owns NBINS/kBlock consecutive bins
-// from the top.  Result in *out (LDS), visible to all threads on return.
-template <int NBINS, class Load>
-__device__ __forceinline__ void find_crossing(Load load, uint32_t target, Cross* out,
+// where load(b) returns h[b].  Thread t owns PER consecutive bins from the
+// top.  Result in *out (LDS), visible to all threads on return.
+template <int NBINS, int BLOCK, class Load>
+__device__ __forceinline__ void find_crossing(Load&& load, uint32_t target, Cross* out,
                                               uint32_t* scan_sm) {
-  constexpr int PER = NBINS / kBlock;
-  static_assert(PER * kBlock == NBINS, "bins per thread");
+  constexpr int PER = NBINS >= BLOCK ? NBINS / BLOCK : 1;
+  constexpr int OWNERS = NBINS / PER;
+  static_assert(PER * OWNERS == NBINS, "bins per thread");
   const int t = threadIdx.x;
   const int hi = NBINS - 1 - t * PER;
   uint32_t c[PER];
   uint32_t s = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    c[i] = load(hi - i);
+    c[i] = (t < OWNERS) ? load(hi - i) : 0u;
     s += c[i];
   }
   uint32_t tot;
-  const uint32_t ex = block_excl_scan(s, scan_sm, tot);
-  if (ex < target && ex + s >= target) {
+  const uint32_t ex = block_excl_scan<BLOCK>(s, scan_sm, tot);
+  if (t < OWNERS && ex < target && ex + s >= target) {
     uint32_t run = ex;
     bool found = false;
 #pragma unroll
@@ -216,16 +297,39 @@ __device__ __forceinline__ void find_crossing(Load load, uint32_t target, Cross*
 
 // Smallest score x (IEEE order over [-inf, +inf]) with vbin(x) >= b, so that
 // for every non-NaN x: vbin(x) >= b  <=>  x >= edge.  vbin is monotone in x,
-// so the set is an up-set; a 64-way search over the order-preserving keys of
-// -inf .. +inf (each round probes 64 evenly spaced keys, one per lane) finds
-// its least element in six rounds.  b <= 0 gives -inf; b >= kBins gives NaN,
-// which no score compares >= to.  Must be called by a whole wave.
+// so the set is an up-set.  The 64 lanes first probe the keys around the
+// arithmetic estimate gmin + b / sc (rounding puts the edge within a few
+// ulps of it); if the edge is not among them, a 64-way search over the keys
+// of -inf .. +inf (six rounds) finds it.  b <= 0 gives -inf; b >= kBins gives
+// NaN, which no score compares >= to.  Must be called by a whole wave.
 __device__ __forceinline__ float bin_edge(int b, float gmin, float sc) {
   if (b <= 0) return -__builtin_inff();
   if (b >= kBins) return __builtin_nanf("");
   uint32_t lo = 0x007FFFFFu;  // key(-inf): vbin = 0 < b
   uint32_t hi = 0xFF800000u;  // key(+inf): vbin = kBins - 1 >= b
   const uint32_t l = (uint32_t)lane_id();
+  {
+    const float est = gmin + (float)b / sc;
+    const uint32_t c = fkey(est);
+    const int64_t pk = (int64_t)c - 31 + (int64_t)l;
+    const uint32_t probe =
+        pk < (int64_t)lo ? lo : (pk > (int64_t)hi ? hi : (uint32_t)pk);
+    const bool ok = vbin(from_key(probe), gmin, sc) >= b;
+    const uint64_t mask = __ballot(ok);
+    if (mask != 0ull && (mask & 1ull) == 0ull) {
+      // the first passing lane is the edge unless probes were clamped
+      const int f = __ffsll((unsigned long long)mask) - 1;
+      const uint32_t e = __shfl(probe, f, 64);
+      const uint32_t below = __shfl(probe, f - 1, 64);
+      if (below + 1u == e) return from_key(e);
+      lo = below;
+      hi = e;
+    } else if (mask == 0ull) {
+      lo = __shfl(probe, 63, 64);
+    } else {
+      hi = __shfl(probe, 0, 64);
+    }
+  }
   while (hi - lo > 1u) {
     const uint32_t span = hi - lo;
     const uint32_t step = span / 64u + ((span & 63u) ? 1u : 0u);
@@ -246,7 +350,9 @@ __device__ __forceinline__ float bin_edge(int b, float gmin, float sc) {
 // generation is read (acquire) before arriving, so a workgroup can never read
 // the flipped value of its own barrier instance.  Spins are bounded: on
 // timeout an error flag is raised in the workspace and the workgroup moves on
-// (results are then undefined, but every wave exits).
+// (results are then undefined, but every wave exits).  What crosses a barrier
+// is read back with agent-scope atomic loads, so no acquire fence (an L2
+// invalidate on this part) is spent after it.
 __device__ __forceinline__ void row_barrier(SlotHeader* hdr, int G, uint32_t* err) {
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -260,8 +366,8 @@ __device__ __forceinline__ void row_barrier(SlotHeader* hdr, int G, uint32_t* er
     } else {
       uint32_t spins = 0;
       while (load_agent(&hdr->bar_gen) == gen) {
-        __builtin_amdgcn_s_sleep(1);
-        if (++spins > (1u << 25)) {
+        __builtin_amdgcn_s_sleep(2);
+        if (++spins > (1u << 24)) {
           atomic_add_agent(err, kErrBarrierTimeout);
           break;
         }
@@ -269,40 +375,183 @@ __device__ __forceinline__ void row_barrier(SlotHeader* hdr, int G, uint32_t* er
     }
   }
   __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+// Count this workgroup as done with its row's slot; true in the last one,
+// which then sees everything the others wrote before counting themselves.
+__device__ __forceinline__ bool finish_slot(SlotHeader* hdr, int G, uint32_t* bc) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    *bc = atomic_add_agent(&hdr->done, 1u);
+  }
+  __syncthreads();
+  const bool last = (*bc == (uint32_t)(G - 1));
+  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return last;
+}
+
+// Row barrier whose last arriver also decides, for the whole row, whether the
+// candidate list can be finished by one workgroup: the verdict travels in the
+// size of the generation step (+1: list usable, +2: rescue), so no extra word
+// needs clearing.  Returns the verdict; *is_last tells the last arriver.
+__device__ __forceinline__ bool row_vote_list_ok(SlotHeader* hdr, int G, uint32_t k, uint32_t* err,
+                                                 uint32_t* bc, bool* is_last) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t gen =
+        __hip_atomic_load(&hdr->bar_gen, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const uint32_t arrived = atomic_add_agent(&hdr->bar_count, 1u);
+    uint32_t ok, last;
+    if (arrived == (uint32_t)(G - 1)) {
+      const uint32_t total = load_agent(&hdr->cand_cur);
+      ok = (total >= k && total <= (uint32_t)kSplitCapMax) ? 1u : 0u;
+      last = 1u;
+      __hip_atomic_store(&hdr->bar_count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&hdr->bar_gen, gen + (ok ? 1u : 2u), __ATOMIC_RELEASE,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      uint32_t spins = 0, now;
+      while ((now = load_agent(&hdr->bar_gen)) == gen) {
+        __builtin_amdgcn_s_sleep(2);
+        if (++spins > (1u << 24)) {
+          atomic_add_agent(err, kErrBarrierTimeout);
+          break;
+        }
+      }
+      ok = (now - gen == 1u) ? 1u : 0u;
+      last = 0u;
+    }
+    bc[0] = ok;
+    bc[1] = last;
+  }
+  __syncthreads();
+  *is_last = bc[1] != 0u;
+  const bool ok = bc[0] != 0u;
+  // only the workgroup that goes on to read the others' candidates needs to
+  // see their plain stores
+  if (ok && *is_last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return ok;
+}
+
+__device__ __forceinline__ void rest_slot(SlotFixed* sf, int t, int block) {
+  for (int i = t; i < 4 * 256; i += block) (&sf->dig[0][0])[i] = 0u;
+  if (t == 0) {
+    sf->hdr.win_cur = 0u;
+    sf->hdr.cand_cur = 0u;
+    sf->hdr.tie_cur = 0u;
+    sf->hdr.done = 0u;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Exact radix selection over an element set
+// ---------------------------------------------------------------------------
+
+struct RSel {
+  uint32_t thr;    // key >> shift of the threshold digit path
+  int shift;       // 24, 16, 8 or 0
+  uint32_t rem;    // how many of the elements with key >> shift == thr to take
+};
+
+// The `need` largest keys among the elements `iter` visits (iter(f) calls
+// f(key) for each element this thread owns): up to four 8-bit digit levels
+// from the top, stopping early when the crossing digit's members are all
+// needed.  Afterwards an element is selected iff key >> shift > thr, or
+// key >> shift == thr and it is one of `rem` such elements.  With `gdig`
+// (split rescue) the digit counts of the row's G workgroups are summed
+// through the workspace behind a barrier at each level.
+template <int BLOCK, bool AGG = false, class Iter>
+__device__ __forceinline__ RSel radix_select(Iter&& iter, uint32_t need, uint32_t* dh, Cross* cross,
+                                             uint32_t* scan, uint32_t* gdig, SlotHeader* hdr, int G,
+                                             uint32_t* err) {
+  const int t = threadIdx.x;
+  uint32_t prefix = 0, rem = need;
+  int shift = 24;
+  for (int L = 0; L < 4; ++L) {
+    shift = 24 - 8 * L;
+    for (int i = t; i < 256; i += BLOCK) dh[i] = 0u;
+    __syncthreads();
+    iter([&](uint32_t key) {
+      const bool act = L == 0 || ((key ^ prefix) >> (shift + 8)) == 0u;
+      if (AGG)
+        lds_inc_agg(dh, (key >> shift) & 255u, act);
+      else if (act)
+        lds_inc(&dh[(key >> shift) & 255u]);
+    });
+    __syncthreads();
+    if (gdig) {
+      uint32_t* gd = gdig + L * 256;
+      for (int i = t; i < 256; i += BLOCK) {
+        const uint32_t c = dh[i];
+        if (c) atomic_add_agent(&gd[i], c);
+      }
+      row_barrier(hdr, G, err);
+      find_crossing<256, BLOCK>([&](int d) { return load_agent(&gd[d]); }, rem, cross, scan);
+    } else {
+      find_crossing<256, BLOCK>([&](int d) { return dh[d]; }, rem, cross, scan);
+    }
+    const Cross c = *cross;
+    prefix |= (uint32_t)c.b << shift;
+    rem -= c.above;
+    if (c.m == rem) break;
+  }
+  return RSel{prefix >> shift, shift, rem};
+}
+
+// Write the selected elements of a list (iter2(f) calls f(key, index) for
+// this thread's elements): those above the threshold digit take consecutive
+// slots from out[gt_base], the first `rem` equal ones (by ticket) from
+// out[eq_base].  `ctr` is two LDS words, zero on entry.
+template <class Iter2>
+__device__ __forceinline__ void emit_list(Iter2&& iter2, const RSel& s, int32_t* out,
+                                          uint32_t gt_base, uint32_t eq_base, uint32_t limit,
+                                          uint32_t* ctr) {
+  iter2([&](uint32_t key, int32_t idx) {
+    const uint32_t d = key >> s.shift;
+    if (d > s.thr) {
+      const uint32_t pos = gt_base + lds_take(&ctr[0]);
+      if (pos < limit) out[pos] = idx;
+    } else if (d == s.thr) {
+      const uint32_t tk = lds_take(&ctr[1]);
+      if (tk < s.rem && eq_base + tk < limit) out[eq_base + tk] = idx;
+    }
+  });
 }
 
 // ---------------------------------------------------------------------------
 // The kernel
 // ---------------------------------------------------------------------------
 
-constexpr int kRankMax = kBlock;  // refine by rank counting up to this many candidates
+constexpr int kRankMax = 256;  // refine by rank counting up to this many candidates
 
-template <int K, int QPT, bool SPLIT>
+template <int BLOCK>
 struct Smem {
-  static constexpr int kCap = SPLIT ? kRankMax : kSingleCap;
   union {
     uint32_t hist[kBins + 64];  // + one trash word per lane for NaN markers
     struct {
-      uint32_t key[kCap];
-      int32_t idx[kCap];
+      uint32_t key[kSingleCap];
+      int32_t idx[kSingleCap];
     } c;
   } u;
   uint32_t dh[256];
-  uint32_t scan[kWaves];
-  float rmin[kWaves];
-  float rmax[kWaves];
+  uint32_t scan[BLOCK / 64];
+  float rmin[BLOCK / 64];
+  float rmax[BLOCK / 64];
   Cross cross;
   float thr[2];
   uint32_t bc[4];
+  uint32_t ctr[4];
 };
 
-template <int K, int QPT, bool SPLIT>
-__global__ void __launch_bounds__(kBlock) gvr_topk_kernel(const GvrParams p) {
-  constexpr int NSB = K / 64;        // sample blocks
-  constexpr int SPW = NSB / kWaves;  // sample blocks per wave
+template <int K, int QPT, int BLOCK, bool SPLIT>
+__global__ void __launch_bounds__(BLOCK) gvr_topk_kernel(const GvrParams p) {
+  constexpr int W = BLOCK / 64;           // waves
+  constexpr int NSB = K / 64;             // sample blocks
+  constexpr int SPW = (NSB + W - 1) / W;  // sample blocks per wave
   constexpr int NW = (QPT * 4 + 31) / 32;
-  __shared__ Smem<K, QPT, SPLIT> sm;
+  __shared__ Smem<BLOCK> sm;
 
   const int t = threadIdx.x;
   const int G = SPLIT ? p.wgs_per_row : 1;
@@ -345,7 +594,7 @@ __global__ void __launch_bounds__(kBlock) gvr_topk_kernel(const GvrParams p) {
 
   // ---- short row (a1): identity then -1 ----------------------------------
   if (nv <= K) {
-    for (int i = g * kBlock + t; i < K; i += G * kBlock) out[i] = (i < nv) ? i : -1;
+    for (int i = g * BLOCK + t; i < K; i += G * BLOCK) out[i] = (i < nv) ? i : -1;
     if (stats && g == 0 && t < kStatsWords)
       stats[t] = (t == 0) ? 0 : (t == 6 ? G : (t == 7 ? p.cap : -1));
     return;
@@ -365,94 +614,84 @@ __global__ void __launch_bounds__(kBlock) gvr_topk_kernel(const GvrParams p) {
   const float* rowp = p.logits + row * (int64_t)S;
   const f4* base = reinterpret_cast<const f4*>(rowp + col0);
 
+  SlotFixed* sf = nullptr;
   SlotHeader* hdr = nullptr;
-  uint32_t* s_key = nullptr;
-  int32_t* s_idx = nullptr;
-  uint32_t* s_wh = nullptr;  // [G][kBins]
-  uint32_t* s_wd = nullptr;  // [G][4][256]
+  uint2* s_pair = nullptr;  // candidate (key, index) pairs
   uint32_t* err = nullptr;
   if (SPLIT) {
-    hdr = reinterpret_cast<SlotHeader*>(p.ws + kWsHeaderBytes) + slot;
-    unsigned char* sb = p.ws + kWsDataOff + (size_t)slot * p.slot_data_bytes;
-    s_key = reinterpret_cast<uint32_t*>(sb + kSlotKeyOff);
-    s_idx = reinterpret_cast<int32_t*>(sb + kSlotIdxOff);
-    s_wh = reinterpret_cast<uint32_t*>(sb + kSlotWgHistOff);
-    s_wd = s_wh + (size_t)G * kBins;
+    sf = reinterpret_cast<SlotFixed*>(p.ws + kWsHeaderBytes) + slot;
+    hdr = &sf->hdr;
+    s_pair = reinterpret_cast<uint2*>(p.ws + kWsDataOff + (size_t)slot * kSlotDataBytes);
     err = reinterpret_cast<uint32_t*>(p.ws);
   }
 
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave index, uniform
   const int l = lane_id();
+  const float qnan = __builtin_nanf("");
 
   // ---- guess (a3): block64 sample over the valid window -------------------
   // Block j starts at floor(j * (nv - 64) / (NSB - 1)); blocks are disjoint
   // for nv > K, so the sample holds exactly K distinct scores, and the first
   // and last blocks touch both ends of the window.  Wave w reads blocks
-  // w, w + kWaves, ...: one 256-byte load per block.
+  // w, w + W, ...: one 256-byte load per block.
   float smp[SPW];
   {
     const float* win = rowp + ks;
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
-      const int j = w + i * kWaves;
-      const int st = (int)(((int64_t)j * (nv - 64)) / (NSB - 1));
-      smp[i] = win[st + l];
+      const int j = w + i * W;
+      if (j < NSB) {
+        const int st = (int)(((int64_t)j * (nv - 64)) / (NSB - 1));
+        smp[i] = win[st + l];
+      } else {
+        smp[i] = qnan;
+      }
     }
   }
 
   // ---- scan (a2): the part, resident in VGPRs -----------------------------
-  // Thread t holds groups q0 + t + j * kBlock, j < QPT: each load instruction
+  // Thread t holds groups q0 + t + j * BLOCK, j < QPT: each load instruction
   // of a wave reads 1 KiB of consecutive scores.  Lanes outside the window or
   // the part (the <= 3 lead lanes, the tail of the last group, groups past the
   // part) become NaN markers here: no selection step accepts a NaN (its
   // compares are false, its histogram increment goes to a trash word, its
   // rescue key is the lowest key), and a genuine -inf tie class stays intact.
-  const float qnan = __builtin_nanf("");
   f4 v[QPT];
 #pragma unroll
   for (int j = 0; j < QPT; ++j) {
-    const int q = q0 + t + j * kBlock;
+    const int q = q0 + t + j * BLOCK;
     if (q < q1) {
       v[j] = __builtin_nontemporal_load(base + q);
     } else {
       v[j] = f4{qnan, qnan, qnan, qnan};
     }
   }
-  {
-    // first group of the window (lead lanes): q == 0 is thread 0's j == 0
-    if (q0 == 0 && t == 0 && lead > 0) {
-#pragma unroll
-      for (int e = 0; e < 3; ++e)
-        if (e < lead) v[0][e] = qnan;
-    }
-    // last group of the window (tail lanes), if it lies in this part
-    const int qlast = Q - 1;
-    const int tail = span - (qlast << 2);  // valid lanes in the last group, 1..4
-    if (tail < 4 && qlast >= q0 && qlast < q1) {
-      const int d = qlast - q0;
-      if ((d % kBlock) == t) {
-        const int jl = d / kBlock;
-#pragma unroll
-        for (int j = 0; j < QPT; ++j)
-          if (j == jl) {
-#pragma unroll
-            for (int e = 1; e < 4; ++e)
-              if (e >= tail) v[j][e] = qnan;
-          }
-      }
-    }
-  }
   // Visit this thread's groups; `full` (uniform per wave) says all 64 lanes
   // hold four in-window scores, so only boundary waves pay for NaN checks.
   auto each = [&](auto&& f) {
+    // An opaque copy of the lane index: every pass recomputes its group
+    // indices instead of the compiler keeping one set live across all passes.
+    int ll = l;
+    asm volatile("" : "+v"(ll));
 #pragma unroll
     for (int j = 0; j < QPT; ++j) {
-      const int qw = q0 + j * kBlock + w * 64;
+      const int qw = q0 + j * BLOCK + w * 64;
       if (qw >= q1) break;
-      const int q = qw + l;
+      const int q = qw + ll;
       const bool full = (qw + 64 <= q1) && (qw > 0 || lead == 0) && ((qw + 64) * 4 <= span);
       f(j, q, full);
     }
+  };
+  auto resident = [&](auto&& f) {
+    each([&](int j, int q, bool) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // opaque copy: the key is recomputed per radix level, not kept live
+        float x = v[j][e];
+        asm volatile("" : "+v"(x));
+        f(rkey(x));
+      }
+    });
   };
 
   // ---- bracket -------------------------------------------------------------
@@ -467,11 +706,12 @@ __global__ void __launch_bounds__(kBlock) gvr_topk_kernel(const GvrParams p) {
     sm.rmin[w] = smin;
     sm.rmax[w] = smax;
   }
-  for (int i = t; i < kBins + 64; i += kBlock) sm.u.hist[i] = 0u;
+  for (int i = t; i < kBins + 64; i += BLOCK) sm.u.hist[i] = 0u;
+  if (t < 4) sm.ctr[t] = 0u;
   __syncthreads();
   float gmin = sm.rmin[0], gmax = sm.rmax[0];
 #pragma unroll
-  for (int i = 1; i < kWaves; ++i) {
+  for (int i = 1; i < W; ++i) {
     gmin = fminf(gmin, sm.rmin[i]);
     gmax = fmaxf(gmax, sm.rmax[i]);
   }
@@ -481,19 +721,169 @@ __global__ void __launch_bounds__(kBlock) gvr_topk_kernel(const GvrParams p) {
                           __builtin_isfinite(range) && __builtin_isfinite(sc) && (sc > 0.0f) &&
                           !p.force_rescue;
 
-  int path = 2;  // 1 fast, 2 rescue (invalid bracket), 3 rescue (overflow)
+  // The lead / tail lanes become NaN markers only now, after the bracket,
+  // so the sample reduction does not wait for the whole part to arrive.
+  {
+    // first group of the window (lead lanes): q == 0 is thread 0's j == 0
+    if (q0 == 0 && t == 0 && lead > 0) {
+#pragma unroll
+      for (int e = 0; e < 3; ++e)
+        if (e < lead) v[0][e] = qnan;
+    }
+    // last group of the window (tail lanes), if it lies in this part
+    const int qlast = Q - 1;
+    const int tail = span - (qlast << 2);  // valid lanes in the last group, 1..4
+    if (tail < 4 && qlast >= q0 && qlast < q1) {
+      const int d = qlast - q0;
+      if ((d % BLOCK) == t) {
+        const int jl = d / BLOCK;
+#pragma unroll
+        for (int j = 0; j < QPT; ++j)
+          if (j == jl) {
+#pragma unroll
+            for (int e = 1; e < 4; ++e)
+              if (e >= tail) v[j][e] = qnan;
+          }
+      }
+    }
+  }
+
+  auto put_stats = [&](int path, int m, int above, int b) {
+    if (stats && t == 0) {
+      stats[0] = path;
+      stats[1] = m;
+      stats[2] = above;
+      stats[3] = b;
+      stats[4] = (int)__float_as_uint(gmin);
+      stats[5] = (int)__float_as_uint(gmax);
+      stats[6] = G;
+      stats[7] = p.cap;
+    }
+  };
+
+  int path = 2;  // 1 fast, 2 rescue (invalid bracket), 3 rescue (crowded top)
   Cross cr{-1, 0u, 0u, 0u};
 
-  // ---- verify (a4, a5): histogram and crossing bin ------------------------
-  if (bracket_ok) {
-    int blo = 0;  // split tier: bins below blo are merged only if needed
-    if (SPLIT) {
-      // Bins the row's K-th value can lie in, from the sample alone: the
-      // sample holds about lam = K*K/nv scores >= the K-th value, so below
-      // the bin where the sample's count from the top reaches lam plus a
-      // wide margin the crossing bin is (almost surely) not found.
-      // Exactness never depends on this: a row whose count above blo falls
-      // short of K merges the remaining bins in a second round.
+  if (!SPLIT) {
+    // ==== one workgroup per row ============================================
+    if (bracket_ok) {
+      // ---- verify (a4, a5): LDS histogram and crossing bin ---------------
+      each([&](int j, int q, bool full) {
+        if (full) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) lds_inc(&sm.u.hist[vbin(v[j][e], gmin, sc)]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x = v[j][e];
+            lds_inc(&sm.u.hist[(x == x) ? vbin(x, gmin, sc) : kBins + l]);
+          }
+        }
+      });
+      __syncthreads();
+      find_crossing<kBins, BLOCK>([&](int b) { return sm.u.hist[b]; }, (uint32_t)K, &sm.cross,
+                                  sm.scan);
+      cr = sm.cross;
+      path = (cr.b >= 0 && cr.m <= (uint32_t)kSingleCap) ? 1 : 3;
+    }
+    if (path == 1) {
+      // ---- compaction (a6) ------------------------------------------------
+      // bin > b*  <=>  x >= x_hi (winner);  bin == b*  <=>  x_lo <= x < x_hi
+      if (w < 2) {
+        const float e = bin_edge(cr.b + w, gmin, sc);
+        if (l == 0) sm.thr[w] = e;
+      }
+      __syncthreads();
+      const uint32_t need = (uint32_t)K - cr.above;
+      uint32_t wb[NW], cb[NW];
+#pragma unroll
+      for (int i = 0; i < NW; ++i) wb[i] = cb[i] = 0u;
+      {
+        const float xlo = sm.thr[0], xhi = sm.thr[1];
+        each([&](int j, int q, bool) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = j * 4 + e;
+            const float x = v[j][e];
+            const bool win = x >= xhi;
+            const bool cand = (x >= xlo) && !win;
+            wb[i >> 5] |= win ? (1u << (i & 31)) : 0u;
+            cb[i >> 5] |= cand ? (1u << (i & 31)) : 0u;
+          }
+        });
+      }
+      uint32_t nwin = 0, ncand = 0;
+#pragma unroll
+      for (int i = 0; i < NW; ++i) {
+        nwin += __popc(wb[i]);
+        ncand += __popc(cb[i]);
+      }
+      uint32_t tot;
+      const uint32_t ex = block_excl_scan<BLOCK>((ncand << 16) | nwin, sm.scan, tot);
+      // winners: walk the set bits (only the index is needed)
+      {
+        uint32_t wpos = ex & 0xFFFFu;
+#pragma unroll
+        for (int d = 0; d < NW; ++d) {
+          uint32_t bits = wb[d];
+          while (bits) {
+            const int i = d * 32 + __builtin_ctz(bits);
+            bits &= bits - 1u;
+            const int q = q0 + t + (i >> 2) * BLOCK;
+            if (wpos < (uint32_t)K) out[wpos] = (q << 2) + (i & 3) - lead;
+            ++wpos;
+          }
+        }
+      }
+      // candidates: few, so whole waves skip groups without any
+      {
+        uint32_t cpos = ex >> 16;
+        each([&](int j, int q, bool) {
+          const uint32_t cq = (cb[(j * 4) >> 5] >> ((j * 4) & 31)) & 0xFu;
+          if (__any(cq != 0u)) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const bool c = (cq >> e) & 1u;
+              if (c && cpos < (uint32_t)kSingleCap) {
+                sm.u.c.key[cpos] = fkey(v[j][e]);
+                sm.u.c.idx[cpos] = (q << 2) + e - lead;
+              }
+              cpos += c ? 1u : 0u;
+            }
+          }
+        });
+      }
+      __syncthreads();
+      // ---- refine (a7) ----------------------------------------------------
+      const uint32_t m = cr.m;
+      if (need == m) {
+        for (uint32_t i = t; i < m; i += BLOCK) out[cr.above + i] = sm.u.c.idx[i];
+      } else if (m <= (uint32_t)kRankMax) {
+        rank_select<BLOCK>(sm.u.c.key, sm.u.c.idx, m, need, out, cr.above);
+      } else {
+        const RSel s = radix_select<BLOCK>(
+            [&](auto&& f) {
+              for (uint32_t i = t; i < m; i += BLOCK) f(sm.u.c.key[i]);
+            },
+            need, sm.dh, &sm.cross, sm.scan, nullptr, nullptr, 1, nullptr);
+        emit_list(
+            [&](auto&& f) {
+              for (uint32_t i = t; i < m; i += BLOCK) f(sm.u.c.key[i], sm.u.c.idx[i]);
+            },
+            s, out, cr.above, cr.above + (need - s.rem), (uint32_t)K, sm.ctr);
+      }
+      put_stats(1, (int)cr.m, (int)cr.above, cr.b);
+      return;
+    }
+  } else {
+    // ==== G workgroups per row =============================================
+    int blo = 0;
+    if (bracket_ok) {
+      // Floor bin from the sample alone: the sample holds about
+      // lam = K*K/nv scores >= the row's K-th value, so the bin where the
+      // sample's count from the top reaches lam plus a wide margin lies at
+      // or below the crossing bin (almost surely; a row where it does not is
+      // caught below and finished exactly all the same).
 #pragma unroll
       for (int i = 0; i < SPW; ++i) {
         const float x = smp[i];
@@ -503,301 +893,188 @@ __global__ void __launch_bounds__(kBlock) gvr_topk_kernel(const GvrParams p) {
       const float lam = (float)K * (float)K / (float)nv;
       const float rl = lam + 4.0f * sqrtf(lam) + 8.0f;
       const uint32_t rlow = rl >= (float)K ? (uint32_t)K : (uint32_t)rl;
-      find_crossing<kBins>([&](int b) { return sm.u.hist[b]; }, rlow, &sm.cross, sm.scan);
-      blo = sm.cross.b > 0 ? sm.cross.b : 0;
-      for (int i = t; i < kBins + 64; i += kBlock) sm.u.hist[i] = 0u;
-      __syncthreads();
+      find_crossing<kBins, BLOCK>([&](int b) { return sm.u.hist[b]; }, rlow, &sm.cross, sm.scan);
+      const Cross sc0 = sm.cross;
+      blo = sc0.b > 0 ? sc0.b : 0;
+      for (int i = t; i < kBins + 64; i += BLOCK) sm.u.hist[i] = 0u;
+      // expected row population of bins >= blo
+      const float pred = (float)(sc0.b >= 0 ? sc0.above + sc0.m : sc0.total) * (float)nv / (float)K;
+      path = (pred <= (float)kPredictMax) ? 1 : 3;
     }
-    each([&](int j, int q, bool full) {
-      if (full) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) lds_inc(&sm.u.hist[vbin(v[j][e], gmin, sc)]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float x = v[j][e];
-          lds_inc(&sm.u.hist[(x == x) ? vbin(x, gmin, sc) : kBins + l]);
-        }
-      }
-    });
-    __syncthreads();
-    if (SPLIT) {
-      // publish this workgroup's bins [blo, kBins) densely, then sum the G
-      // slices of every bin after the barrier
-      uint32_t* mine = s_wh + (size_t)g * kBins;
-      for (int b = blo + t; b < kBins; b += kBlock) mine[b] = sm.u.hist[b];
-      row_barrier(hdr, G, err);
-      auto merged = [&](int b) -> uint32_t {
-        uint32_t s = 0;
-        for (int gg = 0; gg < G; ++gg) s += s_wh[(size_t)gg * kBins + b];
-        return s;
-      };
-      find_crossing<kBins>([&](int b) { return b >= blo ? merged(b) : 0u; }, (uint32_t)K,
-                           &sm.cross, sm.scan);
-      if (sm.cross.b < 0 && blo > 0) {
-        // the sample's estimate was too high: merge the remaining bins
-        for (int b = t; b < blo; b += kBlock) mine[b] = sm.u.hist[b];
-        row_barrier(hdr, G, err);
-        find_crossing<kBins>(merged, (uint32_t)K, &sm.cross, sm.scan);
-      }
-    } else {
-      find_crossing<kBins>([&](int b) { return sm.u.hist[b]; }, (uint32_t)K, &sm.cross, sm.scan);
-    }
-    cr = sm.cross;
-    path = (cr.b >= 0 && cr.m <= (uint32_t)p.cap) ? 1 : 3;
-  }
-
-  if (path == 1) {
-    // ---- compaction (a6) --------------------------------------------------
-    // bin > b*  <=>  x >= x_hi (winner);  bin == b*  <=>  x_lo <= x < x_hi.
-    if (w < 2) {
-      const float e = bin_edge(cr.b + w, gmin, sc);
-      if (l == 0) sm.thr[w] = e;
-    }
-    __syncthreads();
-    const uint32_t need = (uint32_t)K - cr.above;
-    uint32_t wb[NW], cb[NW];
-#pragma unroll
-    for (int i = 0; i < NW; ++i) wb[i] = cb[i] = 0u;
-    {
-      const float xlo = sm.thr[0], xhi = sm.thr[1];
-      each([&](int j, int q, bool) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = j * 4 + e;
-          const float x = v[j][e];
-          const bool win = x >= xhi;
-          const bool cand = (x >= xlo) && !win;
-          wb[i >> 5] |= win ? (1u << (i & 31)) : 0u;
-          cb[i >> 5] |= cand ? (1u << (i & 31)) : 0u;
-        }
-      });
-    }
-    uint32_t nwin = 0, ncand = 0;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) {
-      nwin += __popc(wb[i]);
-      ncand += __popc(cb[i]);
-    }
-    uint32_t tot;
-    const uint32_t ex = block_excl_scan((ncand << 16) | nwin, sm.scan, tot);
-    uint32_t wbase = 0, cbase = 0;
-    if (SPLIT) {
-      if (t == 0) {
-        sm.bc[0] = atomic_add_agent(&hdr->win_cur, tot & 0xFFFFu);
-        sm.bc[1] = atomic_add_agent(&hdr->cand_cur, tot >> 16);
+    if (path == 1) {
+      // ---- compaction of bins >= blo (a6) ---------------------------------
+      if (w == 0) {
+        const float e = bin_edge(blo, gmin, sc);
+        if (l == 0) sm.thr[0] = e;
       }
       __syncthreads();
-      wbase = sm.bc[0];
-      cbase = sm.bc[1];
-    }
-    // winners: walk the set bits (only the index is needed)
-    {
-      uint32_t wpos = wbase + (ex & 0xFFFFu);
+      uint32_t cb[NW];
 #pragma unroll
-      for (int d = 0; d < NW; ++d) {
-        uint32_t bits = wb[d];
-        while (bits) {
-          const int i = d * 32 + __builtin_ctz(bits);
-          bits &= bits - 1u;
-          const int q = q0 + t + (i >> 2) * kBlock;
-          if (wpos < (uint32_t)K) out[wpos] = (q << 2) + (i & 3) - lead;
-          ++wpos;
-        }
-      }
-    }
-    // candidates: few, so whole waves skip groups without any
-    {
-      uint32_t cpos = cbase + (ex >> 16);
-      const uint32_t ccap = SPLIT ? (uint32_t)kSplitCapMax : (uint32_t)kSingleCap;
-      each([&](int j, int q, bool) {
-        const uint32_t cq = (cb[(j * 4) >> 5] >> ((j * 4) & 31)) & 0xFu;
-        if (__any(cq != 0u)) {
+      for (int i = 0; i < NW; ++i) cb[i] = 0u;
+      {
+        const float xlo = sm.thr[0];
+        each([&](int j, int q, bool) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const bool c = (cq >> e) & 1u;
-            if (c && cpos < ccap) {
-              const uint32_t key = fkey(v[j][e]);
-              const int32_t idx = (q << 2) + e - lead;
-              if (SPLIT) {
-                s_key[cpos] = key;
-                s_idx[cpos] = idx;
-              } else {
-                sm.u.c.key[cpos] = key;
-                sm.u.c.idx[cpos] = idx;
+            const int i = j * 4 + e;
+            cb[i >> 5] |= (v[j][e] >= xlo) ? (1u << (i & 31)) : 0u;
+          }
+        });
+      }
+      uint32_t ncand = 0;
+#pragma unroll
+      for (int i = 0; i < NW; ++i) ncand += __popc(cb[i]);
+      uint32_t tot;
+      const uint32_t ex = block_excl_scan<BLOCK>(ncand, sm.scan, tot);
+      if (t == 0) sm.bc[1] = atomic_add_agent(&hdr->cand_cur, tot);
+      __syncthreads();
+      {
+        // Stage this workgroup's candidates in LDS in list order, then write
+        // them out as consecutive 8-byte pairs (coalesced), in rounds of
+        // kSingleCap.
+        const uint32_t base = sm.bc[1];
+        for (uint32_t r0 = 0; r0 < tot; r0 += (uint32_t)kSingleCap) {
+          uint32_t lpos = ex;
+          each([&](int j, int q, bool) {
+            const uint32_t cq = (cb[(j * 4) >> 5] >> ((j * 4) & 31)) & 0xFu;
+            if (__any(cq != 0u)) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const bool c = (cq >> e) & 1u;
+                if (c && lpos >= r0 && lpos < r0 + (uint32_t)kSingleCap) {
+                  float x = v[j][e];
+                  asm volatile("" : "+v"(x));  // keep the key out of the round loop
+                  sm.u.c.key[lpos - r0] = fkey(x);
+                  sm.u.c.idx[lpos - r0] = (q << 2) + e - lead;
+                }
+                lpos += c ? 1u : 0u;
               }
+            } else {
+              lpos += (uint32_t)__popc(cq);
             }
-            cpos += c ? 1u : 0u;
+          });
+          __syncthreads();
+          const uint32_t n = (tot - r0) < (uint32_t)kSingleCap ? (tot - r0) : (uint32_t)kSingleCap;
+          for (uint32_t i = t; i < n; i += BLOCK) {
+            const uint32_t gp = base + r0 + i;
+            if (gp < (uint32_t)kSplitCapMax)
+              s_pair[gp] = make_uint2(sm.u.c.key[i], (uint32_t)sm.u.c.idx[i]);
           }
+          __syncthreads();
         }
-      });
-    }
-
-    // ---- refine (a7) ------------------------------------------------------
-    bool refine_here = !SPLIT;
-    if (SPLIT) {
-      __syncthreads();
-      if (t == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        sm.bc[2] = atomic_add_agent(&hdr->done, 1u);
       }
-      __syncthreads();
-      refine_here = (sm.bc[2] == (uint32_t)(G - 1));
-      if (refine_here) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    } else {
-      __syncthreads();
-    }
-    if (refine_here) {
-      const uint32_t m = cr.m;
-      const uint32_t* keys = SPLIT ? s_key : sm.u.c.key;
-      const int32_t* idxs = SPLIT ? s_idx : sm.u.c.idx;
-      if (need == m) {
-        for (uint32_t i = t; i < m; i += kBlock) out[cr.above + i] = idxs[i];
-      } else if (m <= (uint32_t)kRankMax) {
-        // Rank counting: candidate i's rank is the number of candidates with
-        // a larger key, or an equal key and a smaller index.  Ranks below
-        // `need` are selected and written in rank order (value descending,
-        // smallest index first inside a tie).
-        if (SPLIT) {
-          if ((uint32_t)t < m) {
-            sm.u.c.key[t] = keys[t];
-            sm.u.c.idx[t] = idxs[t];
-          }
-          __syncthreads();
-        }
-        if ((uint32_t)t < m) {
-          const uint32_t kk = sm.u.c.key[t];
-          const int32_t ii = sm.u.c.idx[t];
-          uint32_t rank = 0;
-          for (uint32_t j = 0; j < m; ++j) {
-            const uint32_t kj = sm.u.c.key[j];
-            const int32_t ij = sm.u.c.idx[j];
-            rank += (kj > kk || (kj == kk && ij < ii)) ? 1u : 0u;
-          }
-          if (rank < need) out[cr.above + rank] = ii;
-        }
-      } else {
-        // exact radix select of the `need` largest keys among m candidates
-        constexpr int CPT = (SPLIT ? kSplitCapMax : kSingleCap) / kBlock;
-        uint32_t prefix = 0, rem = need;
-        int shift = 24;
-        for (int L = 0; L < 4; ++L) {
-          shift = 24 - 8 * L;
-          sm.dh[t] = 0u;
-          __syncthreads();
-          for (uint32_t i = t; i < m; i += kBlock) {
-            const uint32_t key = keys[i];
-            if (L == 0 || ((key ^ prefix) >> (shift + 8)) == 0u)
-              lds_inc(&sm.dh[(key >> shift) & 255u]);
-          }
-          __syncthreads();
-          find_crossing<256>([&](int d) { return sm.dh[d]; }, rem, &sm.cross, sm.scan);
-          const Cross c = sm.cross;
-          prefix |= (uint32_t)c.b << shift;
-          rem -= c.above;
-          if (c.m == rem) break;
-        }
-        // emit: above the threshold digit -> taken; equal -> first `rem` by ticket
-        const uint32_t thr = prefix >> shift;
-        uint64_t gtm = 0, eqm = 0;
+      bool last;
+      if (row_vote_list_ok(hdr, G, (uint32_t)K, err, sm.bc, &last)) {
+        if (!last) return;
+        // ---- last workgroup: crossing bin over the candidates (a5) --------
+        // The list holds every score of the row in bins >= blo, so its
+        // histogram is the row's histogram on those bins.  Pairs are read in
+        // batches of CB per thread so the loads overlap.
+        constexpr int CB = 8;
+        const uint32_t total = load_agent(&hdr->cand_cur);
+        for (int i = t; i < kBins + 64; i += BLOCK) sm.u.hist[i] = 0u;
+        __syncthreads();
+        for (uint32_t i0 = 0; i0 < total; i0 += CB * BLOCK) {
+          uint32_t kk[CB];
 #pragma unroll
-        for (int k2 = 0; k2 < CPT; ++k2) {
-          const uint32_t i = t + (uint32_t)k2 * kBlock;
-          if (i < m) {
-            const uint32_t d = keys[i] >> shift;
-            gtm |= (d > thr) ? (1ull << k2) : 0ull;
-            eqm |= (d == thr) ? (1ull << k2) : 0ull;
+          for (int u = 0; u < CB; ++u) {
+            const uint32_t i = i0 + t + u * BLOCK;
+            kk[u] = i < total ? s_pair[i].x : 0u;
+          }
+#pragma unroll
+          for (int u = 0; u < CB; ++u)
+            if (i0 + t + u * BLOCK < total) lds_inc(&sm.u.hist[vbin(from_key(kk[u]), gmin, sc)]);
+        }
+        __syncthreads();
+        find_crossing<kBins, BLOCK>([&](int b) { return sm.u.hist[b]; }, (uint32_t)K, &sm.cross,
+                                    sm.scan);
+        cr = sm.cross;
+        const uint32_t m = cr.m;
+        const uint32_t need = (uint32_t)K - cr.above;
+        const bool in_lds = m <= (uint32_t)kSingleCap;
+        // winners straight out; crossing-bin members to LDS (if they fit)
+        for (uint32_t i0 = 0; i0 < total; i0 += CB * BLOCK) {
+          uint2 pr[CB];
+#pragma unroll
+          for (int u = 0; u < CB; ++u) {
+            const uint32_t i = i0 + t + u * BLOCK;
+            pr[u] = i < total ? s_pair[i] : make_uint2(0u, 0u);
+          }
+#pragma unroll
+          for (int u = 0; u < CB; ++u) {
+            const bool ok = i0 + t + u * BLOCK < total;
+            const int b = vbin(from_key(pr[u].x), gmin, sc);
+            const bool win = ok && b > cr.b;
+            const bool mem = ok && b == cr.b && in_lds;
+            const uint32_t wp = wave_append(win, &sm.ctr[0]);
+            if (win && wp < (uint32_t)K) out[wp] = (int32_t)pr[u].y;
+            const uint32_t mp = wave_append(mem, &sm.ctr[1]);
+            if (mem && mp < (uint32_t)kSingleCap) {
+              sm.u.c.key[mp] = pr[u].x;
+              sm.u.c.idx[mp] = (int32_t)pr[u].y;
+            }
           }
         }
-        const uint32_t ngt = (uint32_t)__popcll(gtm), neq = (uint32_t)__popcll(eqm);
-        uint32_t tot2;
-        const uint32_t ex2 = block_excl_scan((neq << 16) | ngt, sm.scan, tot2);
-        uint32_t gpos = cr.above + (ex2 & 0xFFFFu);
-        uint32_t tk = ex2 >> 16;
-        const uint32_t eqbase = cr.above + (need - rem);
-#pragma unroll
-        for (int k2 = 0; k2 < CPT; ++k2) {
-          const uint32_t i = t + (uint32_t)k2 * kBlock;
-          const bool gt = (gtm >> k2) & 1ull;
-          const bool eq = (eqm >> k2) & 1ull;
-          if (gt && gpos < (uint32_t)K) out[gpos] = idxs[i];
-          if (eq && tk < rem) out[eqbase + tk] = idxs[i];
-          gpos += gt ? 1u : 0u;
-          tk += eq ? 1u : 0u;
+        __syncthreads();
+        if (t < 2) sm.ctr[t] = 0u;
+        __syncthreads();
+        // ---- refine (a7) --------------------------------------------------
+        if (in_lds && need == m) {
+          for (uint32_t i = t; i < m; i += BLOCK) out[cr.above + i] = sm.u.c.idx[i];
+        } else if (in_lds && m <= (uint32_t)kRankMax) {
+          rank_select<BLOCK>(sm.u.c.key, sm.u.c.idx, m, need, out, cr.above);
+        } else if (in_lds) {
+          const RSel s = radix_select<BLOCK>(
+              [&](auto&& f) {
+                for (uint32_t i = t; i < m; i += BLOCK) f(sm.u.c.key[i]);
+              },
+              need, sm.dh, &sm.cross, sm.scan, nullptr, nullptr, 1, nullptr);
+          emit_list(
+              [&](auto&& f) {
+                for (uint32_t i = t; i < m; i += BLOCK) f(sm.u.c.key[i], sm.u.c.idx[i]);
+              },
+              s, out, cr.above, cr.above + (need - s.rem), (uint32_t)K, sm.ctr);
+        } else {
+          // the crossing bin's members, picked out of the list by their bin
+          const int bs = cr.b;
+          auto members = [&](auto&& f) {
+            for (uint32_t i = t; i < total; i += BLOCK) {
+              const uint2 pr = s_pair[i];
+              if (vbin(from_key(pr.x), gmin, sc) == bs) f(pr.x, (int32_t)pr.y);
+            }
+          };
+          const RSel s = radix_select<BLOCK>(
+              [&](auto&& f) { members([&](uint32_t key, int32_t) { f(key); }); }, need, sm.dh,
+              &sm.cross, sm.scan, nullptr, nullptr, 1, nullptr);
+          emit_list(members, s, out, cr.above, cr.above + (need - s.rem), (uint32_t)K, sm.ctr);
         }
+        rest_slot(sf, t, BLOCK);
+        put_stats(1, (int)cr.m, (int)cr.above, cr.b);
+        return;
       }
+      // The list missed the sample's prediction (fewer than K scores above
+      // the floor, or more than it holds): the row's workgroups, whose parts
+      // are still resident, take the parallel rescue together.
+      path = 4;
     }
-    if (SPLIT && refine_here) {
-      // last workgroup: put the slot's counters back at rest
-      if (t == 0) {
-        hdr->win_cur = 0u;
-        hdr->cand_cur = 0u;
-        hdr->tie_cur = 0u;
-        hdr->done = 0u;
-      }
-    }
-    if (stats && (SPLIT ? refine_here : true) && t == 0) {
-      stats[0] = 1;
-      stats[1] = (int)cr.m;
-      stats[2] = (int)cr.above;
-      stats[3] = cr.b;
-      stats[4] = (int)__float_as_uint(gmin);
-      stats[5] = (int)__float_as_uint(gmax);
-      stats[6] = G;
-      stats[7] = p.cap;
-    }
-    return;
   }
 
   // ---- rescue (a8): exact radix select over the whole row -----------------
   {
-    uint32_t prefix = 0, rem = (uint32_t)K;
-    int shift = 24;
-    for (int L = 0; L < 4; ++L) {
-      shift = 24 - 8 * L;
-      sm.dh[t] = 0u;
-      __syncthreads();
-      each([&](int j, int q, bool) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t key = rkey(v[j][e]);
-          if (L == 0 || ((key ^ prefix) >> (shift + 8)) == 0u)
-            lds_inc(&sm.dh[(key >> shift) & 255u]);
-        }
-      });
-      __syncthreads();
-      if (SPLIT) {
-        // publish this workgroup's digit counts densely; sum the G slices
-        s_wd[((size_t)g * 4 + L) * 256 + t] = sm.dh[t];
-        row_barrier(hdr, G, err);
-        find_crossing<256>(
-            [&](int d) {
-              uint32_t s = 0;
-              for (int gg = 0; gg < G; ++gg) s += s_wd[((size_t)gg * 4 + L) * 256 + d];
-              return s;
-            },
-            rem, &sm.cross, sm.scan);
-      } else {
-        find_crossing<256>([&](int d) { return sm.dh[d]; }, rem, &sm.cross, sm.scan);
-      }
-      const Cross c = sm.cross;
-      prefix |= (uint32_t)c.b << shift;
-      rem -= c.above;
-      if (c.m == rem) break;
-    }
-    const uint32_t thr = prefix >> shift;
+    const RSel s = radix_select<BLOCK, true>(resident, (uint32_t)K, sm.dh, &sm.cross, sm.scan,
+                                       SPLIT ? &sf->dig[0][0] : nullptr, hdr, G, err);
     uint32_t ngt = 0, neq = 0;
     each([&](int j, int q, bool) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t d = rkey(v[j][e]) >> shift;
-        ngt += (d > thr) ? 1u : 0u;
-        neq += (d == thr) ? 1u : 0u;
+        const uint32_t d = rkey(v[j][e]) >> s.shift;
+        ngt += (d > s.thr) ? 1u : 0u;
+        neq += (d == s.thr) ? 1u : 0u;
       }
     });
-    if (t == 0) sm.bc[3] = thr;
+    if (t == 0) sm.bc[3] = s.thr;
     uint32_t tot;
-    const uint32_t ex = block_excl_scan((neq << 16) | ngt, sm.scan, tot);
+    const uint32_t ex = block_excl_scan<BLOCK>((neq << 16) | ngt, sm.scan, tot);
     uint32_t gbase = 0, ebase = 0;
     if (SPLIT) {
       if (t == 0) {
@@ -810,51 +1087,31 @@ __global__ void __launch_bounds__(kBlock) gvr_topk_kernel(const GvrParams p) {
     }
     uint32_t gpos = gbase + (ex & 0xFFFFu);
     uint32_t tk = ebase + (ex >> 16);
-    const uint32_t eqbase = (uint32_t)K - rem;
+    const uint32_t eqbase = (uint32_t)K - s.rem;
     // re-read after the scan's barriers so the counting pass's compares are
     // not kept live across it
     const uint32_t thr2 = sm.bc[3];
     each([&](int j, int q, bool) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t d = rkey(v[j][e]) >> shift;
+        const uint32_t d = rkey(v[j][e]) >> s.shift;
         const bool gt = d > thr2;
         const bool eq = d == thr2;
         const int32_t idx = (q << 2) + e - lead;
         if (gt && gpos < (uint32_t)K) out[gpos] = idx;
-        if (eq && tk < rem) out[eqbase + tk] = idx;
+        if (eq && tk < s.rem) out[eqbase + tk] = idx;
         gpos += gt ? 1u : 0u;
         tk += eq ? 1u : 0u;
       }
     });
     bool last = true;
     if (SPLIT) {
-      __syncthreads();
-      if (t == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        sm.bc[2] = atomic_add_agent(&hdr->done, 1u);
-      }
-      __syncthreads();
-      last = (sm.bc[2] == (uint32_t)(G - 1));
-      if (last) {
-        if (t == 0) {
-          hdr->win_cur = 0u;
-          hdr->cand_cur = 0u;
-          hdr->tie_cur = 0u;
-          hdr->done = 0u;
-        }
-      }
+      last = finish_slot(hdr, G, &sm.bc[2]);
+      if (last) rest_slot(sf, t, BLOCK);
     }
-    if (stats && last && t == 0) {
-      stats[0] = path;
-      stats[1] = bracket_ok ? (int)cr.m : -1;
-      stats[2] = bracket_ok ? (int)cr.above : -1;
-      stats[3] = bracket_ok ? cr.b : -1;
-      stats[4] = (int)__float_as_uint(gmin);
-      stats[5] = (int)__float_as_uint(gmax);
-      stats[6] = G;
-      stats[7] = p.cap;
-    }
+    if (last)
+      put_stats(path, bracket_ok && !SPLIT ? (int)cr.m : -1, bracket_ok && !SPLIT ? (int)cr.above : -1,
+                bracket_ok && !SPLIT ? cr.b : -1);
   }
 }
 
@@ -862,26 +1119,33 @@ __global__ void __launch_bounds__(kBlock) gvr_topk_kernel(const GvrParams p) {
 // Host-side dispatch over the instantiated shapes
 // ---------------------------------------------------------------------------
 
-template <int K, int QPT, bool SPLIT>
+template <int K, int QPT, int BLOCK, bool SPLIT>
 static const void* kernel_ptr() {
-  return reinterpret_cast<const void*>(&gvr_topk_kernel<K, QPT, SPLIT>);
+  return reinterpret_cast<const void*>(&gvr_topk_kernel<K, QPT, BLOCK, SPLIT>);
 }
 
-template <int K, bool SPLIT>
-static const void* pick_qpt(int qpt) {
-  switch (qpt) {
-    case 4: return kernel_ptr<K, 4, SPLIT>();
-    case 8: return kernel_ptr<K, 8, SPLIT>();
-    case 17: return kernel_ptr<K, 17, SPLIT>();
-    default: return nullptr;
+template <int K>
+static const void* pick(int block, int qpt, bool split) {
+  if (split) {
+    if (block != kSplitBlock) return nullptr;
+    switch (qpt) {
+      case 4: return kernel_ptr<K, 4, kSplitBlock, true>();
+      case 8: return kernel_ptr<K, 8, kSplitBlock, true>();
+      case 17: return kernel_ptr<K, 17, kSplitBlock, true>();
+      default: return nullptr;
+    }
   }
+  if (block == 256 && qpt == 8) return kernel_ptr<K, 8, 256, false>();
+  if (block == 512 && qpt == 9) return kernel_ptr<K, 9, 512, false>();
+  if (block == 1024 && qpt == 9) return kernel_ptr<K, 9, 1024, false>();
+  return nullptr;
 }
 
-const void* gvr_kernel(int k, int qpt, bool split) {
+const void* gvr_kernel(int k, int block, int qpt, bool split) {
   switch (k) {
-    case 512: return split ? pick_qpt<512, true>(qpt) : pick_qpt<512, false>(qpt);
-    case 1024: return split ? pick_qpt<1024, true>(qpt) : pick_qpt<1024, false>(qpt);
-    case 2048: return split ? pick_qpt<2048, true>(qpt) : pick_qpt<2048, false>(qpt);
+    case 512: return pick<512>(block, qpt, split);
+    case 1024: return pick<1024>(block, qpt, split);
+    case 2048: return pick<2048>(block, qpt, split);
     default: return nullptr;
   }
 }

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string.h>
 
@@ -11,7 +12,7 @@
 #include "gvr_common.h"
 
 namespace ert {
-const void* gvr_kernel(int k, int qpt, bool split);
+const void* gvr_kernel(int k, int block, int qpt, bool split);
 }
 
 using namespace ert;
@@ -22,8 +23,9 @@ bool k_ok(int32_t k) { return k == 512 || k == 1024 || k == 2048; }
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 struct Plan {
-  int G = 1;             // workgroups per row
-  int qpt = 4;           // float4 groups per thread
+  int G = 1;        // workgroups per row
+  int block = 256;  // workgroup size
+  int qpt = 4;      // float4 groups per thread
   int rows_per_launch = 0;
   int launches = 0;
   size_t ws_bytes = 0;
@@ -31,53 +33,71 @@ struct Plan {
   int xcd_group = 0;
 };
 
-int64_t quads_for(int64_t env_len) {
-  // A window of env_len floats starting at any ks spans at most this many
-  // aligned float4 groups (lead <= 3 plus a partial last group).
-  return (env_len + 3 + 3) / 4;
-}
+// A window of env_len floats starting at any ks spans at most this many
+// aligned float4 groups (lead <= 3 plus a partial last group).
+int64_t quads_for(int64_t env_len) { return (env_len + 3 + 3) / 4; }
 
-int smallest_qpt(int64_t quads_per_part) {
-  for (int q : kQptList)
-    if ((int64_t)kBlock * q >= quads_per_part) return q;
-  return 0;
-}
+// Work to fill the chip: about 512 wave quartets (256-thread groups) in
+// flight.
+constexpr int64_t kFillUnits = 512;
 
 // Launch shape for (rows, envelope, k).  `capacity` = workgroups the device
 // keeps resident at once for the split kernel (only the split tier needs its
-// workgroups co-resident, for its row barriers).
+// workgroups co-resident, for the rescue's row barriers).
 int make_plan(int32_t num_rows, int64_t env_len, int32_t k, int32_t force_g, int64_t capacity,
               Plan* pl) {
   Plan p;
   const int64_t Qmax = quads_for(env_len < 1 ? 1 : env_len);
-  const int64_t one_wg_quads = (int64_t)kBlock * kQptMax;
+  // smallest one-workgroup variant that holds the window
+  int single = -1;
+  for (int i = 0; i < (int)(sizeof(kSingleVariants) / sizeof(kSingleVariants[0])); ++i)
+    if ((int64_t)kSingleVariants[i].block * kSingleVariants[i].qpt >= Qmax) {
+      single = i;
+      break;
+    }
   int G;
   if (force_g > 0) {
     if (force_g > kMaxWgsPerRow) return TOPK_EINVAL;
     G = force_g;
+    if (G == 1 && single < 0) return TOPK_EINVAL;  // row does not fit one workgroup
+  } else if (single >= 0 &&
+             (int64_t)num_rows * (kSingleVariants[single].block / 256) >= kFillUnits) {
+    G = 1;  // enough rows to fill the chip with whole rows
   } else {
-    const int64_t g_min = (Qmax + one_wg_quads - 1) / one_wg_quads;
-    // aim for ~512 workgroups in flight, but never parts below 4 groups/thread
-    const int64_t target = 512;
-    const int64_t g_fill = (target + num_rows - 1) / (num_rows > 0 ? num_rows : 1);
-    const int64_t g_useful = (Qmax + (int64_t)kBlock * 4 - 1) / ((int64_t)kBlock * 4);
+    const int64_t part_max = (int64_t)kSplitBlock * kSplitQpt[2];
+    const int64_t g_min = (Qmax + part_max - 1) / part_max;
+    const int64_t g_fill = (kFillUnits + num_rows - 1) / (num_rows > 0 ? num_rows : 1);
+    // never parts below 4 groups per thread
+    const int64_t g_useful = (Qmax + (int64_t)kSplitBlock * 4 - 1) / ((int64_t)kSplitBlock * 4);
     int64_t gg = g_fill < g_useful ? g_fill : g_useful;
     if (gg < g_min) gg = g_min;
     if (gg < 1) gg = 1;
     if (gg > kMaxWgsPerRow) return TOPK_EINVAL;  // row longer than the largest plan
     G = (int)gg;
   }
-  const int64_t per_part = (Qmax + G - 1) / G;
-  const int qpt = smallest_qpt(per_part);
-  if (qpt == 0) return TOPK_EINVAL;  // forced G too small for this row length
   p.G = G;
-  p.qpt = qpt;
   if (G == 1) {
+    if (single < 0) {
+      // one part of the split kernel would need G > 1
+      return TOPK_EINVAL;
+    }
+    p.block = kSingleVariants[single].block;
+    p.qpt = kSingleVariants[single].qpt;
     p.rows_per_launch = num_rows;
     p.launches = num_rows > 0 ? 1 : 0;
     p.ws_bytes = 0;
     p.cap = kSingleCap;
   } else {
+    const int64_t per_part = (Qmax + G - 1) / G;
+    int qpt = 0;
+    for (int q : kSplitQpt)
+      if ((int64_t)kSplitBlock * q >= per_part) {
+        qpt = q;
+        break;
+      }
+    if (qpt == 0) return TOPK_EINVAL;  // forced G too small for this row length
+    p.block = kSplitBlock;
+    p.qpt = qpt;
     int64_t rpl = capacity / G;
     if (rpl > kMaxSlots) rpl = kMaxSlots;
     if (rpl > num_rows) rpl = num_rows;
@@ -86,14 +106,13 @@ int make_plan(int32_t num_rows, int64_t env_len, int32_t k, int32_t force_g, int
     p.launches = num_rows > 0 ? (int)((num_rows + rpl - 1) / rpl) : 0;
     // slots are padded to a multiple of 8 when a row's workgroups share an XCD
     p.xcd_group = (rpl >= 8) ? 1 : 0;
-    const int64_t slots = p.xcd_group ? ((rpl + 7) / 8) * 8 : rpl;
-    if (p.xcd_group && slots * G > capacity) p.xcd_group = 0;
-    const int64_t nslots = p.xcd_group ? slots : rpl;
-    p.ws_bytes = ws_bytes_for((int)nslots, G);
-    int64_t cap = (int64_t)G * kSplitCapPerWg;
-    if (cap > 32LL * k) cap = 32LL * k;
-    if (cap > kSplitCapMax) cap = kSplitCapMax;
-    p.cap = (int)cap;
+    int64_t slots = p.xcd_group ? ((rpl + 7) / 8) * 8 : rpl;
+    if (p.xcd_group && (slots * G > capacity || slots > kMaxSlots)) {
+      p.xcd_group = 0;
+      slots = rpl;
+    }
+    p.ws_bytes = ws_bytes_for((int)slots);
+    p.cap = kSplitCapMax;
   }
   *pl = p;
   return TOPK_OK;
@@ -107,7 +126,8 @@ size_t ws_bytes_upper(int32_t num_rows, int64_t env_len, int32_t k, int32_t forc
   if (p.G == 1) return 0;
   int64_t rpl = num_rows < kMaxSlots ? num_rows : kMaxSlots;
   int64_t slots = ((rpl + 7) / 8) * 8;
-  return ws_bytes_for((int)slots, p.G);
+  if (slots > kMaxSlots) slots = kMaxSlots;
+  return ws_bytes_for((int)slots);
 }
 
 int validate(int mode, const void* logits, int64_t row_stride, const void* e1, const void* e2,
@@ -126,7 +146,10 @@ struct DevInfo {
   bool probed = false;
   bool ok = false;
   int cus = 0;
-  int occ[3][3] = {};  // [k idx][qpt idx] split-kernel workgroups per CU
+  int occ[3][3] = {};      // [k idx][split qpt idx] split-kernel workgroups per CU
+  int occ_api[3][3] = {};  // what hipOccupancyMaxActiveBlocksPerMultiprocessor says
+  int regs[3][3] = {};     // VGPRs per thread of each split kernel
+  int lds[3][3] = {};      // static LDS bytes
   void* slab = nullptr;
   size_t slab_bytes = 0;
 };
@@ -135,7 +158,11 @@ DevInfo g_dev[kMaxDev];
 std::mutex g_mu;
 
 int kidx(int k) { return k == 512 ? 0 : (k == 1024 ? 1 : 2); }
-int qidx(int q) { return q == 4 ? 0 : (q == 8 ? 1 : 2); }
+int qidx(int q) {
+  for (int i = 0; i < 3; ++i)
+    if (kSplitQpt[i] == q) return i;
+  return 0;
+}
 
 int device_info(DevInfo** out, int* dev_out) {
   int dev = 0;
@@ -150,11 +177,30 @@ int device_info(DevInfo** out, int* dev_out) {
     for (int ki = 0; ki < 3; ++ki)
       for (int qi = 0; qi < 3; ++qi) {
         const int ks[3] = {512, 1024, 2048};
+        const void* f = gvr_kernel(ks[ki], kSplitBlock, kSplitQpt[qi], true);
         int nb = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &nb, gvr_kernel(ks[ki], kQptList[qi], true), kBlock, 0) != hipSuccess)
-          nb = 1;
-        d.occ[ki][qi] = nb > 0 ? nb : 1;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, f, kSplitBlock, 0) != hipSuccess)
+          nb = 0;
+        d.occ_api[ki][qi] = nb;
+        // Residency from the kernel's own resources and the gfx950 compute
+        // unit: 4 SIMDs with 512 VGPRs per lane each (granule 8), at most 8
+        // waves per SIMD, 160 KiB of LDS.  Taken as the smaller of this and
+        // the runtime's figure when the latter is available, so the split
+        // tier never plans more co-resident workgroups than both allow.
+        hipFuncAttributes at;
+        int mine = 1;
+        if (hipFuncGetAttributes(&at, f) == hipSuccess) {
+          const int v = at.numRegs > 0 ? ((at.numRegs + 7) / 8) * 8 : 512;
+          const int waves_simd = std::min(8, 512 / v);
+          const int wg_waves = kSplitBlock / 64;
+          const int by_vgpr = (4 * waves_simd) / wg_waves;
+          const int lds = (int)at.sharedSizeBytes;
+          const int by_lds = lds > 0 ? (160 * 1024) / lds : 64;
+          mine = std::max(1, std::min(by_vgpr, by_lds));
+          d.regs[ki][qi] = at.numRegs;
+          d.lds[ki][qi] = lds;
+        }
+        d.occ[ki][qi] = (nb > 0) ? std::min(nb, mine) : mine;
       }
   }
   if (!d.ok) return TOPK_EDEVICE;
@@ -218,7 +264,7 @@ int run(int mode, const float* logits, int64_t row_stride, const int32_t* e1, co
     }
   }
 
-  const void* kern = gvr_kernel(k, pl.qpt, pl.G > 1);
+  const void* kern = gvr_kernel(k, pl.block, pl.qpt, pl.G > 1);
   if (!kern) return TOPK_EINVAL;
   GvrParams prm;
   memset(&prm, 0, sizeof(prm));
@@ -233,7 +279,6 @@ int run(int mode, const float* logits, int64_t row_stride, const int32_t* e1, co
   prm.indices = indices;
   prm.row_stats = opts ? opts->row_stats : nullptr;
   prm.ws = ws;
-  prm.slot_data_bytes = slot_data_bytes(pl.G);
   for (int64_t r0 = 0; r0 < num_rows; r0 += pl.rows_per_launch) {
     const int64_t nr = (num_rows - r0) < pl.rows_per_launch ? (num_rows - r0) : pl.rows_per_launch;
     prm.row_begin = (int32_t)r0;
@@ -247,7 +292,7 @@ int run(int mode, const float* logits, int64_t row_stride, const int32_t* e1, co
       grid = prm.xcd_group ? ((nr + 7) / 8) * 8 * pl.G : nr * pl.G;
     }
     void* args[] = {&prm};
-    if (hipLaunchKernel(kern, dim3((unsigned)grid), dim3(kBlock), args, 0, stream) != hipSuccess)
+    if (hipLaunchKernel(kern, dim3((unsigned)grid), dim3(pl.block), args, 0, stream) != hipSuccess)
       return TOPK_ELAUNCH;
   }
   if (hipGetLastError() != hipSuccess) return TOPK_ELAUNCH;
@@ -327,6 +372,25 @@ int topk_plan_query(int32_t num_rows, int64_t row_stride, int64_t max_row_len, i
   out[3] = pl.launches;
   out[4] = (int64_t)pl.ws_bytes;
   out[5] = pl.cap;
+  out[6] = pl.block;
+  return TOPK_OK;
+}
+
+int topk_device_query(int64_t* out) {
+  if (!out) return TOPK_EINVAL;
+  std::lock_guard<std::mutex> lock(g_mu);
+  DevInfo* d = nullptr;
+  int dev = 0;
+  const int rc = device_info(&d, &dev);
+  if (rc != TOPK_OK) return rc;
+  out[0] = d->cus;
+  for (int ki = 0; ki < 3; ++ki)
+    for (int qi = 0; qi < 3; ++qi) {
+      out[1 + ki * 3 + qi] = d->occ[ki][qi];
+      out[10 + ki * 3 + qi] = d->occ_api[ki][qi];
+      out[19 + ki * 3 + qi] = d->regs[ki][qi];
+      out[28 + ki * 3 + qi] = d->lds[ki][qi];
+    }
   return TOPK_OK;
 }
 

@@ -119,8 +119,11 @@ const char* topk_strerror(int status);
  *      exact radix rescue runs on every long row.
  *  row_stats: optional device int32[num_rows][TOPK_STATS_WORDS]; per row:
  *      [0] path (0 short, 1 bracket + refine, 2 rescue: invalid bracket,
- *          3 rescue: crossing bin over the candidate cap),
- *      [1] m (crossing-bin population, -1 if no histogram ran),
+ *          3 rescue: crowded crossing region -- the crossing bin over the
+ *          candidate cap, or (split rows) a sample predicting it -- and
+ *          4 split row finished by one workgroup from memory because its
+ *          candidate list missed the sample's prediction),
+ *      [1] m (crossing-bin population, -1 if not computed),
  *      [2] above (count in bins above the crossing bin, -1 if none),
  *      [3] crossing bin index (-1 if none),
  *      [4] bit pattern of the sample minimum, [5] of the sample maximum,
@@ -144,14 +147,23 @@ int topk_prefill_ex(const float* logits, int64_t row_stride, const int32_t* row_
                     hipStream_t stream, const topk_options* opts);
 
 /* Host-only planning and validation, callable without a GPU.  Fills
- * out[0..5] = {workgroups per row, quads per thread, rows per launch,
- * launches, workspace bytes, candidate cap} for the shapes given (the same
+ * out[0..6] = {workgroups per row, float4 groups per thread, rows per launch,
+ * launches, workspace bytes, candidate cap, workgroup size} for the shapes
+ * given (the same
  * plan topk_decode / topk_prefill would use; `force_wgs_per_row` as in
  * topk_options; `cu_count` and `wgs_per_cu` stand in for the device's resident
  * capacity).  Returns a status code. */
 int topk_plan_query(int32_t num_rows, int64_t row_stride, int64_t max_row_len, int32_t k,
                     int32_t force_wgs_per_row, int32_t cu_count, int32_t wgs_per_cu,
                     int64_t* out);
+
+/* Facts about the current device the planner uses (out holds 37 values):
+ * out[0] = compute units; for k = {512, 1024, 2048}[ki] and the qi-th split
+ * variant, out[1 + 3*ki + qi] = resident split-tier workgroups per compute
+ * unit the planner uses, out[10 + ..] = the runtime occupancy figure,
+ * out[19 + ..] = VGPRs per thread, out[28 + ..] = static LDS bytes.
+ * Returns a status. */
+int topk_device_query(int64_t* out);
 
 /* Host-side argument validation exactly as the entry points run it (no device
  * access).  mode: 0 decode (extents = n_valid, extents2 unused), 1 prefill. */

@@ -105,14 +105,14 @@ def test_workspace_bytes():
 def test_plans_for_the_workloads():
     # many short-to-mid rows: one workgroup per row, whole window resident
     p = ert.plan_query(4096, 16640, 1024)
-    assert p["wgs_per_row"] == 1 and p["quads_per_thread"] * 256 * 4 >= 16640 + 6
+    assert p["wgs_per_row"] == 1 and p["quads_per_thread"] * p["block"] * 4 >= 16640 + 6
     # few long rows: split, the row's parts cover the whole stride
     for rows, stride, k in ((64, 131072, 2048), (1, 131072, 512), (8, 131072, 512),
                             (8, 262144, 2048)):
         p = ert.plan_query(rows, stride, k)
-        assert p["wgs_per_row"] > 1
+        assert p["wgs_per_row"] > 1 and p["block"] == 256
         assert p["wgs_per_row"] * p["quads_per_thread"] * 256 >= (stride + 6) // 4
-        assert p["cap"] == min(p["wgs_per_row"] * 4096, 32 * k, 16384)
+        assert p["cap"] == 16384
     # capacity bounds rows per launch (co-resident split workgroups)
     p = ert.plan_query(64, 131072, 2048, cu_count=16, wgs_per_cu=2)
     assert p["rows_per_launch"] * p["wgs_per_row"] <= 32 and p["launches"] > 1

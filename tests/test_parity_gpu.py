@@ -60,8 +60,13 @@ def test_tie_heavy_paths(ert):
     assert_parity(w, got)
     kinds = list(workloads.TIE_ROW_KINDS)
     assert st[kinds.index("all_equal"), 0] == 2            # collapsed bracket -> rescue
-    assert st[kinds.index("dense_bin40k"), 0] == 3         # 40K in the crossing bin -> rescue
-    assert st[kinds.index("dense_bin40k"), 1] > st[kinds.index("dense_bin40k"), 7]
+    r6 = kinds.index("dense_bin40k")
+    assert st[r6, 0] == 3                                   # 40K in the crossing region -> rescue
+    assert st[r6, 1] == -1 or st[r6, 1] > st[r6, 7]
+    log(f"[paths] {dict(zip(kinds, st[:, 0].tolist()))}")
+    # sorted rows defeat the floor estimate (the sample's blocks are runs of
+    # equal values): the list misses and the parallel rescue finishes the row
+    assert st[kinds.index("quantised64_sorted"), 0] in (3, 4)
 
 
 # ---- tiers must agree ------------------------------------------------------------
