@@ -65,7 +65,7 @@ def traffic_for(workload_name: str):
     return ent.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, budget_s: float = 1.5):
+def cpu_baseline(w, budget_s: float = 10.0):
     """Time the oracle on the host (all cores) over whole batches, bounded."""
     import oracle
     cores = oracle.online_cores()
@@ -77,7 +77,7 @@ def cpu_baseline(w, budget_s: float = 1.5):
         reps += 1
         rows += w.num_rows
         el = time.perf_counter() - t0
-        if el >= budget_s or reps >= 50:
+        if el >= budget_s:
             break
     return {
         "value": rows / el,
@@ -86,6 +86,20 @@ def cpu_baseline(w, budget_s: float = 1.5):
         "kind": "oracle",
         "sample": f"{reps} full batch(es) of {w.name} ({rows} rows, {el:.2f} s wall on {cores} threads)",
     }
+
+
+def copy_calib(torch, steps: int):
+    """A plain device copy of known size: 256 MiB read, 256 MiB written per
+    launch.  Its FETCH_SIZE / WRITE_SIZE counter readings give the scale from
+    counter units to bytes for the top-K kernel's readings."""
+    n = 64 << 20
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(max(steps, 1)):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calib_bytes_read": n * 4, "copy_calib_bytes_written": n * 4,
+                      "launches": max(steps, 1)}), flush=True)
 
 
 def main():
@@ -97,6 +111,10 @@ def main():
     ap.add_argument("--bs", type=int, default=1, help="batch size for workload 4")
     ap.add_argument("--warm", action="store_true", help="no rotation: inputs stay cache-resident")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline leg")
+    ap.add_argument("--eager", action="store_true",
+                    help="time eager launches instead of a graph replay (for counter runs)")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="run only a plain 256 MiB device copy, the counter scale reference")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -105,6 +123,10 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calib:
+        copy_calib(torch, args.steps)
+        return
 
     import exact_row_top_amd as ert
     import workloads
@@ -143,26 +165,37 @@ def main():
     # Timed region: the K launches, captured once as a HIP graph and replayed
     # between one pair of events, so the per-call host cost of the Python
     # binding does not gap the GPU (the same graph-replay protocol the pages'
-    # warm and cold tables use).  Copies rotate inside the graph.
-    cap = torch.cuda.Stream()
-    cap.wait_stream(torch.cuda.current_stream())
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(cap):
-        with torch.cuda.graph(graph, stream=cap):
-            for i in range(args.steps):
-                step(args.warmup + i)
-    torch.cuda.synchronize()
-    graph.replay()  # untimed: first replay pays any one-time graph setup
-    torch.cuda.synchronize()
+    # warm and cold tables use).  Copies rotate inside the graph.  With
+    # --eager the K launches are issued one by one behind a GPU sleep instead.
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    t_start.record()
-    graph.replay()
-    t_end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    if args.eager:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        torch.cuda._sleep(int(20e6))
+        t_start.record()
+        for i in range(args.steps):
+            step(args.warmup + i)
+        t_end.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    else:
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(graph, stream=cap):
+                for i in range(args.steps):
+                    step(args.warmup + i)
+        torch.cuda.synchronize()
+        graph.replay()  # untimed: first replay pays any one-time graph setup
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        t_start.record()
+        graph.replay()
+        t_end.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     region_us = t_start.elapsed_time(t_end) * 1e3
     ms_per_step = region_us / args.steps / 1e3
     mean_launch_us = region_us / args.steps
@@ -214,6 +247,7 @@ def main():
         "p99_us_per_row": float(np.percentile(per, 99)) / rows,
         "p50_us_per_launch": float(np.percentile(per, 50)),
         "p99_us_per_launch": float(np.percentile(per, 99)),
+        "timing": "eager launches" if args.eager else "graph replay",
         "roofline": {
             "bound": "hbm",
             "achieved": achieved,
