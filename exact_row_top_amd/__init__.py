@@ -65,6 +65,8 @@ def load_library():
     lib.topk_plan_query.restype = ctypes.c_int
     lib.topk_device_query.argtypes = [ctypes.POINTER(I64)]
     lib.topk_device_query.restype = ctypes.c_int
+    lib.topk_workspace_layout.argtypes = [ctypes.POINTER(I64)]
+    lib.topk_workspace_layout.restype = ctypes.c_int
     lib.topk_validate.argtypes = [I32, P, I64, P, P, I32, I32, P, P, SZ, I64]
     lib.topk_validate.restype = ctypes.c_int
     _lib = lib
@@ -92,6 +94,15 @@ def plan_query(num_rows: int, row_stride: int, k: int, force_wgs_per_row: int = 
                                           cu_count, wgs_per_cu, out))
     keys = ("wgs_per_row", "quads_per_thread", "rows_per_launch", "launches", "workspace_bytes",
             "cap", "block")
+    return dict(zip(keys, (int(x) for x in out)))
+
+
+def workspace_layout() -> dict:
+    """Byte layout of a split-tier workspace (host-only)."""
+    out = (ctypes.c_int64 * 6)()
+    _check(load_library().topk_workspace_layout(out))
+    keys = ("header_bytes", "slot_fixed_bytes", "slots", "data_offset", "slice_bytes",
+            "list_bytes")
     return dict(zip(keys, (int(x) for x in out)))
 
 

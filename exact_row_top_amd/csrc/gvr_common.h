@@ -17,15 +17,10 @@ constexpr int kBins = 2048;
 // final refine).
 constexpr int kSingleCap = 2048;
 
-// Per-row candidate storage of the split tier (workspace).  The pages' rescue
-// trigger is m > min(CS x 4096, 32 x K, 16384) with CS workgroups per row
-// (PR 20998 "What changes"); 16384 is its ceiling.
-constexpr int kSplitCapMax = 16384;
-constexpr int kSplitCapPerWg = 4096;
-
-// Split tier: a row whose sampled count above the floor bin predicts more
-// than this many scores there goes straight to the parallel rescue.
-constexpr int kPredictMax = kSplitCapMax / 2;
+// The pages' rescue trigger is a crossing bin of more than
+// min(CS x 4096, 32 x K, 16384) members with CS workgroups per row
+// (PR 20998 "What changes").  Here the crossing-bin members of a row go
+// through LDS for the refine in both tiers, so the trigger is m > kSingleCap.
 
 // Launch variants: (workgroup size, float4 groups per thread).
 struct Variant {
@@ -44,36 +39,42 @@ constexpr int kStatsWords = 8;
 
 // Workspace layout (bytes):
 //   [0, 256)                             error flags (word 0)
-//   kMaxSlots fixed blocks of 4352 bytes: SlotHeader + digit counts [4][256]
-//   then one data block per slot: candidate (key, index) pairs
-//   [kSplitCapMax]; consecutive blocks are skewed by 4 KiB so the slots'
-//   first bytes do not all land on the same memory channels
-// The fixed blocks hold every word that carries state between calls, and the
-// last workgroup of a row returns them to zero (only the barrier generation
-// keeps counting); their place does not depend on the plan, so one workspace
-// serves any plan it is large enough for.  Data blocks are written before they
+//   kMaxSlots fixed blocks of 12544 bytes: SlotHeader, digit counts [4][256],
+//   value histogram [kBins]
+//   then one data block per slot: G slices of kBins suffix counts (slice g:
+//   workgroup g's count of scores in bins >= b), then the crossing bin's
+//   members as (key, index) pairs [kSingleCap]
+// The fixed blocks hold every word that carries state between workgroups, and
+// the last workgroup of a row returns them all to zero; their place does not
+// depend on the plan, so one workspace serves any plan it is large enough for.  Data blocks are written before they
 // are read and need no clearing.
 struct SlotHeader {
-  uint32_t bar_count;  // barrier arrivals (returns to 0 after each barrier)
-  uint32_t bar_gen;    // barrier generation (monotone, never reset)
+  uint32_t bar_count;  // barrier arrivals of the current row
   uint32_t done;       // workgroups finished with the slot (last one cleans)
-  uint32_t win_cur;    // winner output cursor
-  uint32_t cand_cur;   // candidate cursor
+  uint32_t win_cur;    // winner output cursor (rescue)
+  uint32_t cand_cur;   // spare cursor
   uint32_t tie_cur;    // tie tickets (rescue)
-  uint32_t pad[58];    // header is 256 bytes
+  uint32_t pad[59];    // header is 256 bytes
 };
 static_assert(sizeof(SlotHeader) == 256, "slot header size");
 
 struct SlotFixed {
   SlotHeader hdr;
   uint32_t dig[4][256];  // rescue digit counts, one row per radix level
+  uint32_t hist[2048];   // the row's value histogram (bins >= the floor bin)
 };
-static_assert(sizeof(SlotFixed) == 4352, "slot fixed block size");
+static_assert(sizeof(SlotFixed) == 12544, "slot fixed block size");
 
 constexpr size_t kWsHeaderBytes = 256;
 constexpr size_t kWsDataOff = kWsHeaderBytes + sizeof(SlotFixed) * kMaxSlots;
-constexpr size_t kSlotDataBytes = 2 * sizeof(uint32_t) * kSplitCapMax + 4096;
-constexpr size_t ws_bytes_for(int slots) { return kWsDataOff + (size_t)slots * kSlotDataBytes; }
+// Per-slot data block of a plan with G workgroups per row: G slices of
+// kBins suffix counts (one per workgroup), then the member list.
+constexpr size_t kSliceBytes = sizeof(uint32_t) * kBins;
+constexpr size_t kListBytes = 2 * sizeof(uint32_t) * kSingleCap;
+constexpr size_t slot_data_bytes(int G) { return (size_t)G * kSliceBytes + kListBytes; }
+constexpr size_t ws_bytes_for(int slots, int G) {
+  return kWsDataOff + (size_t)slots * slot_data_bytes(G);
+}
 
 // Error flags written by the kernel into workspace word 0.
 constexpr uint32_t kErrBarrierTimeout = 1u;

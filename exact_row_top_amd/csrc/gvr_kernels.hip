@@ -28,16 +28,16 @@
 //  * G workgroups per row (SPLIT = true): each keeps 1/G of the row resident.
 //    Every workgroup derives the same bracket and, from the sample's own
 //    histogram, the same floor bin b_lo below which the crossing bin (almost
-//    surely) is not; it appends its scores in bins >= b_lo to the row's
-//    candidate list with one atomic and counts itself done.  The last
-//    workgroup histograms that list -- the row's histogram restricted to
-//    bins >= b_lo, so the crossing bin, `above` and m are exactly those of
-//    the full histogram -- and selects.  No workgroup waits for another on
-//    this path.  Rows whose sample predicts a crowded top (tie-heavy rows)
-//    and rows with an invalid bracket take the parallel rescue, whose radix
-//    levels merge through the workspace with a generation barrier.  A row the
-//    prediction missed (the list overflows, or holds fewer than K) is
-//    finished by the last workgroup alone from the row in memory.
+//    surely) is not.  Each counts its part's scores in bins >= b_lo in LDS
+//    and adds those counts into the row's histogram in the workspace; after
+//    one barrier every workgroup reads the merged counts and finds the same
+//    crossing bin, writes its own winners straight to the output (one
+//    cursor per row) and its crossing-bin members to a short list; the last
+//    workgroup to finish refines that list.  A row whose merged counts do
+//    not reach K (the floor was too high), whose crossing bin is crowded, or
+//    whose bracket is invalid takes the parallel rescue with all its
+//    workgroups, the radix levels merging through the workspace behind the
+//    same kind of barrier.
 //
 // Ordering: scores compare as IEEE values with -0 == +0; the order-preserving
 // key maps a float to a uint32 whose unsigned order is that value order.
@@ -72,15 +72,29 @@ __device__ __forceinline__ float from_key(uint32_t k) {
 // while the row holds K non-NaN scores.
 __device__ __forceinline__ uint32_t rkey(float x) { return (x == x) ? fkey(x) : 0u; }
 
-// Histogram bin of x over the bracket: clamp((x - gmin) * sc, 0, kBins - 1),
-// truncated.  Monotone non-decreasing in x, equal values share a bin, and it
-// is the single definition every step uses (the build disables FP
-// contraction, so no step can evaluate it differently).  The final mask only
-// matters for NaN (outside the contract): it keeps the LDS index in range.
-__device__ __forceinline__ int vbin(float x, float gmin, float sc) {
-  float t = (x - gmin) * sc;
+// The bracket's bin map: bin(x) = trunc(clamp(fma(x, sc, c0), 0, kBins - 1))
+// with sc = kBins / (gmax - gmin) and c0 = -gmin * sc, each rounded once per
+// row.  A fused multiply-add is monotone non-decreasing in x, so equal values
+// share a bin and bins ascend with the value; this is the single definition
+// every step uses.  The same map scaled by 4 (exact: a power-of-two scale)
+// gives a bin's LDS byte offset directly.  The final masks only matter for
+// NaN (outside the contract): they keep the LDS index in range.
+struct BinMap {
+  float gmin, sc, c0, sc4, c04;
+};
+__device__ __forceinline__ int vbin(float x, const BinMap& bm) {
+  float t = __builtin_fmaf(x, bm.sc, bm.c0);
   t = __builtin_amdgcn_fmed3f(t, 0.0f, (float)(kBins - 1));
   return ((int)t) & (kBins - 1);
+}
+__device__ __forceinline__ uint32_t vbin_off(float x, const BinMap& bm) {
+  float t = __builtin_fmaf(x, bm.sc4, bm.c04);
+  t = __builtin_amdgcn_fmed3f(t, 0.0f, (float)(4 * (kBins - 1)));
+  return ((uint32_t)(int)t) & (uint32_t)(4 * kBins - 4);
+}
+// LDS histogram word at a byte offset from vbin_off.
+__device__ __forceinline__ uint32_t* hword(uint32_t* h, uint32_t off) {
+  return reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(h) + off);
 }
 
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
@@ -88,6 +102,15 @@ __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 __device__ __forceinline__ uint32_t atomic_add_agent(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void atomic_add_agent_nr(uint32_t* p, uint32_t v) {
+  (void)__hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until this wave's vector memory operations (stores, atomics) have
+// completed: s_waitcnt vmcnt(0) (gfx9 encoding: expcnt and lgkmcnt fields at
+// their no-wait maxima).  Every wave runs it before the workgroup barrier
+// that precedes one thread's release and arrival, so what all waves wrote is
+// performed before any other workgroup can see the arrival.
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 __device__ __forceinline__ uint32_t load_agent(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -98,21 +121,22 @@ __device__ __forceinline__ uint32_t lds_take(uint32_t* p) {
   return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// Count one per active lane into h[d]; when every active lane of the wave
+// Count one per lane with `act` into h[d]; when every such lane of the wave
 // has the same d (tie-heavy rows), one lane adds them all at once instead of
-// 64 conflicting increments.  Must be reached by the whole wave.
+// 64 conflicting increments.  The first lane's d comes from readfirstlane
+// (no LDS round trip).  Must be reached by the whole wave.
 __device__ __forceinline__ void lds_inc_agg(uint32_t* h, uint32_t d, bool act) {
-  const uint64_t am = __ballot(act);
-  if (am == 0ull) return;
-  const int fl = __ffsll((unsigned long long)am) - 1;
-  const uint32_t d0 = __shfl(d, fl, 64);
-  const uint64_t same = __ballot(act && d == d0);
-  if (same == am) {
-    if (lane_id() == fl)
-      __hip_atomic_fetch_add(&h[d0], (uint32_t)__popcll(am), __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_WORKGROUP);
-  } else if (act) {
-    __hip_atomic_fetch_add(&h[d], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  if (act) {
+    const uint32_t d0 = __builtin_amdgcn_readfirstlane(d);
+    const uint64_t am = __ballot(1);
+    const uint64_t same = __ballot(d == d0);
+    if (same == am) {
+      if ((uint32_t)lane_id() == (uint32_t)(__ffsll((unsigned long long)am) - 1))
+        __hip_atomic_fetch_add(&h[d0], (uint32_t)__popcll(am), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
+    } else {
+      __hip_atomic_fetch_add(&h[d], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
   }
 }
 
@@ -225,6 +249,18 @@ __device__ __forceinline__ void wave_minmax(float& mn, float& mx) {
 
 // Exclusive prefix sum over the block in thread order; `total` gets the sum.
 // `sm` holds BLOCK/64 words.  Contains two __syncthreads.
+// Exclusive offsets of v over the whole workgroup in an arbitrary wave order:
+// a wave prefix sum and one LDS add per wave on *ctr (zero beforehand).  No
+// workgroup barrier.  Must be reached by the whole wave.
+__device__ __forceinline__ uint32_t wave_offsets(uint32_t v, uint32_t* ctr) {
+  const uint32_t inc = wave_incl_scan(v);
+  uint32_t base = 0u;
+  if (lane_id() == 63)
+    base = __hip_atomic_fetch_add(ctr, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  base = (uint32_t)__builtin_amdgcn_readlane((int)base, 63);
+  return base + inc - v;
+}
+
 template <int BLOCK>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sm, uint32_t& total) {
   constexpr int W = BLOCK / 64;
@@ -302,19 +338,19 @@ __device__ __forceinline__ void find_crossing(Load&& load, uint32_t target, Cros
 // ulps of it); if the edge is not among them, a 64-way search over the keys
 // of -inf .. +inf (six rounds) finds it.  b <= 0 gives -inf; b >= kBins gives
 // NaN, which no score compares >= to.  Must be called by a whole wave.
-__device__ __forceinline__ float bin_edge(int b, float gmin, float sc) {
+__device__ __forceinline__ float bin_edge(int b, const BinMap& bm) {
   if (b <= 0) return -__builtin_inff();
   if (b >= kBins) return __builtin_nanf("");
   uint32_t lo = 0x007FFFFFu;  // key(-inf): vbin = 0 < b
   uint32_t hi = 0xFF800000u;  // key(+inf): vbin = kBins - 1 >= b
   const uint32_t l = (uint32_t)lane_id();
   {
-    const float est = gmin + (float)b / sc;
+    const float est = bm.gmin + (float)b / bm.sc;
     const uint32_t c = fkey(est);
     const int64_t pk = (int64_t)c - 31 + (int64_t)l;
     const uint32_t probe =
         pk < (int64_t)lo ? lo : (pk > (int64_t)hi ? hi : (uint32_t)pk);
-    const bool ok = vbin(from_key(probe), gmin, sc) >= b;
+    const bool ok = vbin(from_key(probe), bm) >= b;
     const uint64_t mask = __ballot(ok);
     if (mask != 0ull && (mask & 1ull) == 0ull) {
       // the first passing lane is the edge unless probes were clamped
@@ -335,7 +371,7 @@ __device__ __forceinline__ float bin_edge(int b, float gmin, float sc) {
     const uint32_t step = span / 64u + ((span & 63u) ? 1u : 0u);
     const uint64_t pk = (uint64_t)lo + (uint64_t)(l + 1u) * step;
     const uint32_t probe = pk >= (uint64_t)hi ? hi : (uint32_t)pk;
-    const bool ok = vbin(from_key(probe), gmin, sc) >= b;
+    const bool ok = vbin(from_key(probe), bm) >= b;
     const uint64_t mask = __ballot(ok);  // lane 63 probes hi, so mask != 0
     const int f = __ffsll((unsigned long long)mask) - 1;
     const uint32_t nhi = __shfl(probe, f, 64);
@@ -346,98 +382,51 @@ __device__ __forceinline__ float bin_edge(int b, float gmin, float sc) {
   return from_key(hi);
 }
 
-// Generation barrier over the G workgroups of one row (split tier).  The
-// generation is read (acquire) before arriving, so a workgroup can never read
-// the flipped value of its own barrier instance.  Spins are bounded: on
-// timeout an error flag is raised in the workspace and the workgroup moves on
-// (results are then undefined, but every wave exits).  What crosses a barrier
-// is read back with agent-scope atomic loads, so no acquire fence (an L2
-// invalidate on this part) is spent after it.
-__device__ __forceinline__ void row_barrier(SlotHeader* hdr, int G, uint32_t* err) {
+
+// Barrier over the G workgroups of one row (split tier).  Arrivals add one
+// to the slot's counter, which only the row's last finishing workgroup
+// returns to zero, so a workgroup's n-th barrier is passed once the counter
+// reaches n * G (`nbar` counts this workgroup's barriers).  Everything that
+// crosses between workgroups is an agent-scope atomic (adds, loads, stores),
+// so no cache write-back or invalidate is needed: each wave only waits for
+// its own atomics to complete before the workgroup arrives.  Spins are
+// bounded: on timeout an error flag is raised in the workspace and the
+// workgroup moves on (results are then undefined, but every wave exits).
+__device__ __forceinline__ void row_barrier(SlotHeader* hdr, int G, uint32_t& nbar, uint32_t* err) {
+  wait_vm();
   __syncthreads();
+  ++nbar;
   if (threadIdx.x == 0) {
-    const uint32_t gen =
-        __hip_atomic_load(&hdr->bar_gen, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    const uint32_t arrived = atomic_add_agent(&hdr->bar_count, 1u);
-    if (arrived == (uint32_t)(G - 1)) {
-      __hip_atomic_store(&hdr->bar_count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&hdr->bar_gen, gen + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-      uint32_t spins = 0;
-      while (load_agent(&hdr->bar_gen) == gen) {
-        __builtin_amdgcn_s_sleep(2);
-        if (++spins > (1u << 24)) {
-          atomic_add_agent(err, kErrBarrierTimeout);
-          break;
-        }
+    atomic_add_agent_nr(&hdr->bar_count, 1u);
+    const uint32_t target = nbar * (uint32_t)G;
+    uint32_t spins = 0;
+    while (load_agent(&hdr->bar_count) < target) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > (1u << 24)) {
+        atomic_add_agent_nr(err, kErrBarrierTimeout);
+        break;
       }
     }
   }
   __syncthreads();
 }
 
-// Count this workgroup as done with its row's slot; true in the last one,
-// which then sees everything the others wrote before counting themselves.
+// Count this workgroup as done with its row's slot; true in the last one.
+// What the others wrote for it (list entries, counters) are agent-scope
+// atomics they completed before counting themselves.
 __device__ __forceinline__ bool finish_slot(SlotHeader* hdr, int G, uint32_t* bc) {
+  wait_vm();
   __syncthreads();
-  if (threadIdx.x == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    *bc = atomic_add_agent(&hdr->done, 1u);
-  }
+  if (threadIdx.x == 0) *bc = atomic_add_agent(&hdr->done, 1u);
   __syncthreads();
-  const bool last = (*bc == (uint32_t)(G - 1));
-  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  return last;
-}
-
-// Row barrier whose last arriver also decides, for the whole row, whether the
-// candidate list can be finished by one workgroup: the verdict travels in the
-// size of the generation step (+1: list usable, +2: rescue), so no extra word
-// needs clearing.  Returns the verdict; *is_last tells the last arriver.
-__device__ __forceinline__ bool row_vote_list_ok(SlotHeader* hdr, int G, uint32_t k, uint32_t* err,
-                                                 uint32_t* bc, bool* is_last) {
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t gen =
-        __hip_atomic_load(&hdr->bar_gen, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    const uint32_t arrived = atomic_add_agent(&hdr->bar_count, 1u);
-    uint32_t ok, last;
-    if (arrived == (uint32_t)(G - 1)) {
-      const uint32_t total = load_agent(&hdr->cand_cur);
-      ok = (total >= k && total <= (uint32_t)kSplitCapMax) ? 1u : 0u;
-      last = 1u;
-      __hip_atomic_store(&hdr->bar_count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&hdr->bar_gen, gen + (ok ? 1u : 2u), __ATOMIC_RELEASE,
-                         __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-      uint32_t spins = 0, now;
-      while ((now = load_agent(&hdr->bar_gen)) == gen) {
-        __builtin_amdgcn_s_sleep(2);
-        if (++spins > (1u << 24)) {
-          atomic_add_agent(err, kErrBarrierTimeout);
-          break;
-        }
-      }
-      ok = (now - gen == 1u) ? 1u : 0u;
-      last = 0u;
-    }
-    bc[0] = ok;
-    bc[1] = last;
-  }
-  __syncthreads();
-  *is_last = bc[1] != 0u;
-  const bool ok = bc[0] != 0u;
-  // only the workgroup that goes on to read the others' candidates needs to
-  // see their plain stores
-  if (ok && *is_last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  return ok;
+  return *bc == (uint32_t)(G - 1);
 }
 
 __device__ __forceinline__ void rest_slot(SlotFixed* sf, int t, int block) {
   for (int i = t; i < 4 * 256; i += block) (&sf->dig[0][0])[i] = 0u;
+  for (int i = t; i < kBins; i += block) sf->hist[i] = 0u;
   if (t == 0) {
+    sf->hdr.bar_count = 0u;
     sf->hdr.win_cur = 0u;
     sf->hdr.cand_cur = 0u;
     sf->hdr.tie_cur = 0u;
@@ -465,7 +454,7 @@ struct RSel {
 template <int BLOCK, bool AGG = false, class Iter>
 __device__ __forceinline__ RSel radix_select(Iter&& iter, uint32_t need, uint32_t* dh, Cross* cross,
                                              uint32_t* scan, uint32_t* gdig, SlotHeader* hdr, int G,
-                                             uint32_t* err) {
+                                             uint32_t& nbar, uint32_t* err) {
   const int t = threadIdx.x;
   uint32_t prefix = 0, rem = need;
   int shift = 24;
@@ -487,7 +476,7 @@ __device__ __forceinline__ RSel radix_select(Iter&& iter, uint32_t need, uint32_
         const uint32_t c = dh[i];
         if (c) atomic_add_agent(&gd[i], c);
       }
-      row_barrier(hdr, G, err);
+      row_barrier(hdr, G, nbar, err);
       find_crossing<256, BLOCK>([&](int d) { return load_agent(&gd[d]); }, rem, cross, scan);
     } else {
       find_crossing<256, BLOCK>([&](int d) { return dh[d]; }, rem, cross, scan);
@@ -527,7 +516,7 @@ __device__ __forceinline__ void emit_list(Iter2&& iter2, const RSel& s, int32_t*
 constexpr int kRankMax = 256;  // refine by rank counting up to this many candidates
 
 template <int BLOCK>
-struct Smem {
+struct alignas(16) Smem {
   union {
     uint32_t hist[kBins + 64];  // + one trash word per lane for NaN markers
     struct {
@@ -545,8 +534,19 @@ struct Smem {
   uint32_t ctr[4];
 };
 
+// Occupancy the one-workgroup variants of up to 512 threads are compiled for
+// (K <= 1024 for 512 threads): eight waves per SIMD (64 VGPRs), so that four
+// 512-thread workgroups share a compute unit.  The others keep the
+// compiler's choice (at 64 VGPRs they would spill).
+template <int K, int BLOCK, bool SPLIT>
+struct WavesPerEu {
+  static constexpr int value = (SPLIT || BLOCK > 512 || (BLOCK == 512 && K > 1024)) ? 1 : 8;
+};
+
 template <int K, int QPT, int BLOCK, bool SPLIT>
-__global__ void __launch_bounds__(BLOCK) gvr_topk_kernel(const GvrParams p) {
+__global__ void __launch_bounds__(BLOCK)
+    __attribute__((amdgpu_waves_per_eu(WavesPerEu<K, BLOCK, SPLIT>::value)))
+    gvr_topk_kernel(const GvrParams p) {
   constexpr int W = BLOCK / 64;           // waves
   constexpr int NSB = K / 64;             // sample blocks
   constexpr int SPW = (NSB + W - 1) / W;  // sample blocks per wave
@@ -616,12 +616,15 @@ __global__ void __launch_bounds__(BLOCK) gvr_topk_kernel(const GvrParams p) {
 
   SlotFixed* sf = nullptr;
   SlotHeader* hdr = nullptr;
-  uint2* s_pair = nullptr;  // candidate (key, index) pairs
+  uint32_t* slices = nullptr;  // per-workgroup suffix counts [G][kBins]
+  uint2* s_pair = nullptr;     // crossing-bin members (key, index)
   uint32_t* err = nullptr;
   if (SPLIT) {
     sf = reinterpret_cast<SlotFixed*>(p.ws + kWsHeaderBytes) + slot;
     hdr = &sf->hdr;
-    s_pair = reinterpret_cast<uint2*>(p.ws + kWsDataOff + (size_t)slot * kSlotDataBytes);
+    unsigned char* data = p.ws + kWsDataOff + (size_t)slot * slot_data_bytes(G);
+    slices = reinterpret_cast<uint32_t*>(data);
+    s_pair = reinterpret_cast<uint2*>(data + (size_t)G * kSliceBytes);
     err = reinterpret_cast<uint32_t*>(p.ws);
   }
 
@@ -707,7 +710,10 @@ __global__ void __launch_bounds__(BLOCK) gvr_topk_kernel(const GvrParams p) {
     sm.rmax[w] = smax;
   }
   for (int i = t; i < kBins + 64; i += BLOCK) sm.u.hist[i] = 0u;
-  if (t < 4) sm.ctr[t] = 0u;
+  if (t < 4) {
+    sm.ctr[t] = 0u;
+    sm.bc[t] = 0u;
+  }
   __syncthreads();
   float gmin = sm.rmin[0], gmax = sm.rmax[0];
 #pragma unroll
@@ -716,10 +722,15 @@ __global__ void __launch_bounds__(BLOCK) gvr_topk_kernel(const GvrParams p) {
     gmax = fmaxf(gmax, sm.rmax[i]);
   }
   const float range = gmax - gmin;
-  const float sc = (float)kBins / range;
+  BinMap bm;
+  bm.gmin = gmin;
+  bm.sc = (float)kBins / range;
+  bm.c0 = -gmin * bm.sc;
+  bm.sc4 = 4.0f * bm.sc;
+  bm.c04 = 4.0f * bm.c0;
   const bool bracket_ok = __builtin_isfinite(gmin) && __builtin_isfinite(gmax) && (gmax > gmin) &&
-                          __builtin_isfinite(range) && __builtin_isfinite(sc) && (sc > 0.0f) &&
-                          !p.force_rescue;
+                          __builtin_isfinite(range) && __builtin_isfinite(bm.sc4) &&
+                          __builtin_isfinite(bm.c04) && (bm.sc > 0.0f) && !p.force_rescue;
 
   // The lead / tail lanes become NaN markers only now, after the bracket,
   // so the sample reduction does not wait for the whole part to arrive.
@@ -761,6 +772,7 @@ __global__ void __launch_bounds__(BLOCK) gvr_topk_kernel(const GvrParams p) {
     }
   };
 
+  uint32_t nbar = 0;  // row barriers this workgroup has passed (split tier)
   int path = 2;  // 1 fast, 2 rescue (invalid bracket), 3 rescue (crowded top)
   Cross cr{-1, 0u, 0u, 0u};
 
@@ -771,12 +783,12 @@ __global__ void __launch_bounds__(BLOCK) gvr_topk_kernel(const GvrParams p) {
       each([&](int j, int q, bool full) {
         if (full) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) lds_inc(&sm.u.hist[vbin(v[j][e], gmin, sc)]);
+          for (int e = 0; e < 4; ++e) lds_inc(hword(sm.u.hist, vbin_off(v[j][e], bm)));
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float x = v[j][e];
-            lds_inc(&sm.u.hist[(x == x) ? vbin(x, gmin, sc) : kBins + l]);
+            lds_inc(hword(sm.u.hist, (x == x) ? vbin_off(x, bm) : 4u * (uint32_t)(kBins + l)));
           }
         }
       });
@@ -790,7 +802,7 @@ __global__ void __launch_bounds__(BLOCK) gvr_topk_kernel(const GvrParams p) {
       // ---- compaction (a6) ------------------------------------------------
       // bin > b*  <=>  x >= x_hi (winner);  bin == b*  <=>  x_lo <= x < x_hi
       if (w < 2) {
-        const float e = bin_edge(cr.b + w, gmin, sc);
+        const float e = bin_edge(cr.b + w, bm);
         if (l == 0) sm.thr[w] = e;
       }
       __syncthreads();
@@ -818,8 +830,10 @@ __global__ void __launch_bounds__(BLOCK) gvr_topk_kernel(const GvrParams p) {
         nwin += __popc(wb[i]);
         ncand += __popc(cb[i]);
       }
-      uint32_t tot;
-      const uint32_t ex = block_excl_scan<BLOCK>((ncand << 16) | nwin, sm.scan, tot);
+      // positions: a wave prefix sum plus one LDS add per wave (winners in
+      // the low half-word, candidates in the high one; the order of the
+      // output and of the candidate list does not matter)
+      const uint32_t ex = wave_offsets((ncand << 16) | nwin, &sm.bc[0]);
       // winners: walk the set bits (only the index is needed)
       {
         uint32_t wpos = ex & 0xFFFFu;
@@ -865,7 +879,7 @@ __global__ void __launch_bounds__(BLOCK) gvr_topk_kernel(const GvrParams p) {
             [&](auto&& f) {
               for (uint32_t i = t; i < m; i += BLOCK) f(sm.u.c.key[i]);
             },
-            need, sm.dh, &sm.cross, sm.scan, nullptr, nullptr, 1, nullptr);
+            need, sm.dh, &sm.cross, sm.scan, nullptr, nullptr, 1, nbar, nullptr);
         emit_list(
             [&](auto&& f) {
               for (uint32_t i = t; i < m; i += BLOCK) f(sm.u.c.key[i], sm.u.c.idx[i]);
@@ -887,7 +901,7 @@ __global__ void __launch_bounds__(BLOCK) gvr_topk_kernel(const GvrParams p) {
 #pragma unroll
       for (int i = 0; i < SPW; ++i) {
         const float x = smp[i];
-        lds_inc(&sm.u.hist[(x == x) ? vbin(x, gmin, sc) : kBins + l]);
+        lds_inc(hword(sm.u.hist, (x == x) ? vbin_off(x, bm) : 4u * (uint32_t)(kBins + l)));
       }
       __syncthreads();
       const float lam = (float)K * (float)K / (float)nv;
@@ -896,173 +910,240 @@ __global__ void __launch_bounds__(BLOCK) gvr_topk_kernel(const GvrParams p) {
       find_crossing<kBins, BLOCK>([&](int b) { return sm.u.hist[b]; }, rlow, &sm.cross, sm.scan);
       const Cross sc0 = sm.cross;
       blo = sc0.b > 0 ? sc0.b : 0;
-      for (int i = t; i < kBins + 64; i += BLOCK) sm.u.hist[i] = 0u;
-      // expected row population of bins >= blo
-      const float pred = (float)(sc0.b >= 0 ? sc0.above + sc0.m : sc0.total) * (float)nv / (float)K;
-      path = (pred <= (float)kPredictMax) ? 1 : 3;
+      // A sample bin at or above the floor holding 8 or more samples marks a
+      // row with heavy ties there: its histogram pass aggregates per wave.
+      for (int i = t; i < kBins + 64; i += BLOCK) {
+        if (i < kBins && i >= blo && sm.u.hist[i] >= 8u) sm.bc[3] = 1u;
+        sm.u.hist[i] = 0u;
+      }
+      path = 1;
     }
     if (path == 1) {
-      // ---- compaction of bins >= blo (a6) ---------------------------------
+      // ---- verify (a4): the row's histogram on bins >= blo ----------------
+      // Each workgroup counts its part's scores >= edge(blo) per bin in LDS,
+      // adds the non-zero counts into the row's histogram in the workspace
+      // and publishes its suffix counts (its scores in bins >= b, for each
+      // b >= blo) in its slice.  After one barrier every workgroup reads the
+      // row's histogram and finds the same crossing bin; the slices of the
+      // workgroups before it say where its winners and members go.  Bins
+      // below blo are not needed: were the crossing bin there, the merged
+      // counts would not reach K and the row would take the rescue.
       if (w == 0) {
-        const float e = bin_edge(blo, gmin, sc);
+        const float e = bin_edge(blo, bm);
         if (l == 0) sm.thr[0] = e;
       }
       __syncthreads();
-      uint32_t cb[NW];
+      const float xf = sm.thr[0];
+      if (sm.bc[3]) {
+        each([&](int j, int q, bool) {
 #pragma unroll
-      for (int i = 0; i < NW; ++i) cb[i] = 0u;
+          for (int e = 0; e < 4; ++e) {
+            const float x = v[j][e];
+            const bool in = x >= xf;
+            lds_inc_agg(sm.u.hist, in ? (uint32_t)vbin(x, bm) : 0u, in);
+          }
+        });
+      } else {
+        // only the lanes whose score reaches the floor take part in each
+        // increment: the LDS cost follows the active lanes
+        each([&](int j, int q, bool) {
+          int b[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x = v[j][e];
+            b[e] = x >= xf ? (int)vbin_off(x, bm) : -1;
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (b[e] >= 0) lds_inc(hword(sm.u.hist, (uint32_t)b[e]));
+        });
+      }
+      __syncthreads();
+      uint32_t* gh = sf->hist;
       {
-        const float xlo = sm.thr[0];
+        constexpr int PER = kBins / BLOCK;
+        const int hi = kBins - 1 - t * PER;
+        uint32_t c[PER];
+        uint32_t sum = 0;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+          c[i] = hi - i >= blo ? sm.u.hist[hi - i] : 0u;
+          sum += c[i];
+        }
+        uint32_t tot;
+        uint32_t run = block_excl_scan<BLOCK>(sum, sm.scan, tot);
+        uint32_t* mine = slices + (size_t)g * kBins;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+          const int b = hi - i;
+          run += c[i];
+          if (b >= blo) {
+            __hip_atomic_store(&mine[b], run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (c[i]) atomic_add_agent_nr(&gh[b], c[i]);
+          }
+        }
+      }
+      row_barrier(hdr, G, nbar, err);
+      {
+        constexpr int BPT = kBins / BLOCK;
+        uint32_t r[BPT];
+#pragma unroll
+        for (int i = 0; i < BPT; ++i) {
+          const int b = t + i * BLOCK;
+          r[i] = b >= blo ? load_agent(&gh[b]) : 0u;
+        }
+#pragma unroll
+        for (int i = 0; i < BPT; ++i) sm.u.hist[t + i * BLOCK] = r[i];
+      }
+      __syncthreads();
+      // ---- crossing bin (a5), the same in every workgroup of the row -----
+      find_crossing<kBins, BLOCK>([&](int b) { return sm.u.hist[b]; }, (uint32_t)K, &sm.cross,
+                                  sm.scan);
+      cr = sm.cross;
+      // Merged counts below K (the sample's floor lay above the K-th value)
+      // or a crowded crossing bin: the row's workgroups take the rescue
+      // together.
+      path = cr.b < 0 ? 4 : (cr.m > (uint32_t)kSingleCap ? 3 : 1);
+    }
+    if (path == 1) {
+      // ---- compaction (a6) --------------------------------------------------
+      // Waves 0 and 1 find the edges of b* and b* + 1; wave 2 sums, over the
+      // workgroups before this one, their winners (scores in bins > b*) and
+      // members (scores in b*) from their slices: this workgroup's winners
+      // take output slots from the first sum on, its members list slots
+      // from the second.
+      if (w < 2) {
+        const float e = bin_edge(cr.b + w, bm);
+        if (l == 0) sm.thr[w] = e;
+      } else if (w == 2) {
+        uint32_t s0 = 0u, s1 = 0u;
+        if (l < g) {
+          const uint32_t* sl = slices + (size_t)l * kBins;
+          if (cr.b + 1 < kBins)
+            s1 = __hip_atomic_load(&sl[cr.b + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          s0 = __hip_atomic_load(&sl[cr.b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        const uint32_t ow = wave_incl_scan(s1);
+        const uint32_t om = wave_incl_scan(s0 - s1);
+        if (l == 63) {
+          sm.bc[0] = ow;
+          sm.bc[1] = om;
+        }
+      }
+      __syncthreads();
+      const uint32_t need = (uint32_t)K - cr.above;
+      const uint32_t m = cr.m;
+      const uint32_t above = cr.above;
+      const bool direct = need == m;  // every member is selected
+      uint32_t wb[NW], cb[NW];
+#pragma unroll
+      for (int i = 0; i < NW; ++i) wb[i] = cb[i] = 0u;
+      {
+        const float xlo = sm.thr[0], xhi = sm.thr[1];
         each([&](int j, int q, bool) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = j * 4 + e;
-            cb[i >> 5] |= (v[j][e] >= xlo) ? (1u << (i & 31)) : 0u;
+            const float x = v[j][e];
+            const bool win = x >= xhi;
+            const bool cand = (x >= xlo) && !win;
+            wb[i >> 5] |= win ? (1u << (i & 31)) : 0u;
+            cb[i >> 5] |= cand ? (1u << (i & 31)) : 0u;
           }
         });
       }
-      uint32_t ncand = 0;
+      uint32_t nwin = 0, ncand = 0;
 #pragma unroll
-      for (int i = 0; i < NW; ++i) ncand += __popc(cb[i]);
-      uint32_t tot;
-      const uint32_t ex = block_excl_scan<BLOCK>(ncand, sm.scan, tot);
-      if (t == 0) sm.bc[1] = atomic_add_agent(&hdr->cand_cur, tot);
-      __syncthreads();
+      for (int i = 0; i < NW; ++i) {
+        nwin += __popc(wb[i]);
+        ncand += __popc(cb[i]);
+      }
+      const uint32_t ex = wave_offsets((ncand << 16) | nwin, &sm.ctr[2]);
       {
-        // Stage this workgroup's candidates in LDS in list order, then write
-        // them out as consecutive 8-byte pairs (coalesced), in rounds of
-        // kSingleCap.
-        const uint32_t base = sm.bc[1];
-        for (uint32_t r0 = 0; r0 < tot; r0 += (uint32_t)kSingleCap) {
-          uint32_t lpos = ex;
-          each([&](int j, int q, bool) {
-            const uint32_t cq = (cb[(j * 4) >> 5] >> ((j * 4) & 31)) & 0xFu;
-            if (__any(cq != 0u)) {
+        uint32_t wpos = sm.bc[0] + (ex & 0xFFFFu);
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const bool c = (cq >> e) & 1u;
-                if (c && lpos >= r0 && lpos < r0 + (uint32_t)kSingleCap) {
-                  float x = v[j][e];
-                  asm volatile("" : "+v"(x));  // keep the key out of the round loop
-                  sm.u.c.key[lpos - r0] = fkey(x);
-                  sm.u.c.idx[lpos - r0] = (q << 2) + e - lead;
-                }
-                lpos += c ? 1u : 0u;
-              }
-            } else {
-              lpos += (uint32_t)__popc(cq);
-            }
-          });
-          __syncthreads();
-          const uint32_t n = (tot - r0) < (uint32_t)kSingleCap ? (tot - r0) : (uint32_t)kSingleCap;
-          for (uint32_t i = t; i < n; i += BLOCK) {
-            const uint32_t gp = base + r0 + i;
-            if (gp < (uint32_t)kSplitCapMax)
-              s_pair[gp] = make_uint2(sm.u.c.key[i], (uint32_t)sm.u.c.idx[i]);
+        for (int d = 0; d < NW; ++d) {
+          uint32_t bits = wb[d];
+          while (bits) {
+            const int i = d * 32 + __builtin_ctz(bits);
+            bits &= bits - 1u;
+            const int q = q0 + t + (i >> 2) * BLOCK;
+            if (wpos < above) out[wpos] = (q << 2) + (i & 3) - lead;
+            ++wpos;
           }
-          __syncthreads();
         }
       }
-      bool last;
-      if (row_vote_list_ok(hdr, G, (uint32_t)K, err, sm.bc, &last)) {
-        if (!last) return;
-        // ---- last workgroup: crossing bin over the candidates (a5) --------
-        // The list holds every score of the row in bins >= blo, so its
-        // histogram is the row's histogram on those bins.  Pairs are read in
-        // batches of CB per thread so the loads overlap.
-        constexpr int CB = 8;
-        const uint32_t total = load_agent(&hdr->cand_cur);
-        for (int i = t; i < kBins + 64; i += BLOCK) sm.u.hist[i] = 0u;
-        __syncthreads();
-        for (uint32_t i0 = 0; i0 < total; i0 += CB * BLOCK) {
-          uint32_t kk[CB];
+      uint64_t* list = reinterpret_cast<uint64_t*>(s_pair);
+      {
+        uint32_t cpos = sm.bc[1] + (ex >> 16);
+        each([&](int j, int q, bool) {
+          const uint32_t cq = (cb[(j * 4) >> 5] >> ((j * 4) & 31)) & 0xFu;
+          if (__any(cq != 0u)) {
 #pragma unroll
-          for (int u = 0; u < CB; ++u) {
+            for (int e = 0; e < 4; ++e) {
+              const bool c = (cq >> e) & 1u;
+              if (c && cpos < m) {
+                const int32_t idx = (q << 2) + e - lead;
+                if (direct) {
+                  out[above + cpos] = idx;
+                } else {
+                  float x = v[j][e];
+                  asm volatile("" : "+v"(x));
+                  const uint64_t pr = ((uint64_t)(uint32_t)idx << 32) | fkey(x);
+                  __hip_atomic_store(&list[cpos], pr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+              }
+              cpos += c ? 1u : 0u;
+            }
+          }
+        });
+      }
+      // ---- refine (a7): the row's last workgroup picks `need` members -----
+      if (!finish_slot(hdr, G, &sm.bc[2])) return;
+      if (!direct) {
+        for (uint32_t i0 = 0; i0 < m; i0 += 4 * BLOCK) {
+          uint64_t r[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
             const uint32_t i = i0 + t + u * BLOCK;
-            kk[u] = i < total ? s_pair[i].x : 0u;
+            r[u] = i < m ? __hip_atomic_load(&list[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                         : 0ull;
           }
 #pragma unroll
-          for (int u = 0; u < CB; ++u)
-            if (i0 + t + u * BLOCK < total) lds_inc(&sm.u.hist[vbin(from_key(kk[u]), gmin, sc)]);
-        }
-        __syncthreads();
-        find_crossing<kBins, BLOCK>([&](int b) { return sm.u.hist[b]; }, (uint32_t)K, &sm.cross,
-                                    sm.scan);
-        cr = sm.cross;
-        const uint32_t m = cr.m;
-        const uint32_t need = (uint32_t)K - cr.above;
-        const bool in_lds = m <= (uint32_t)kSingleCap;
-        // winners straight out; crossing-bin members to LDS (if they fit)
-        for (uint32_t i0 = 0; i0 < total; i0 += CB * BLOCK) {
-          uint2 pr[CB];
-#pragma unroll
-          for (int u = 0; u < CB; ++u) {
+          for (int u = 0; u < 4; ++u) {
             const uint32_t i = i0 + t + u * BLOCK;
-            pr[u] = i < total ? s_pair[i] : make_uint2(0u, 0u);
-          }
-#pragma unroll
-          for (int u = 0; u < CB; ++u) {
-            const bool ok = i0 + t + u * BLOCK < total;
-            const int b = vbin(from_key(pr[u].x), gmin, sc);
-            const bool win = ok && b > cr.b;
-            const bool mem = ok && b == cr.b && in_lds;
-            const uint32_t wp = wave_append(win, &sm.ctr[0]);
-            if (win && wp < (uint32_t)K) out[wp] = (int32_t)pr[u].y;
-            const uint32_t mp = wave_append(mem, &sm.ctr[1]);
-            if (mem && mp < (uint32_t)kSingleCap) {
-              sm.u.c.key[mp] = pr[u].x;
-              sm.u.c.idx[mp] = (int32_t)pr[u].y;
+            if (i < m) {
+              sm.u.c.key[i] = (uint32_t)r[u];
+              sm.u.c.idx[i] = (int32_t)(r[u] >> 32);
             }
           }
         }
         __syncthreads();
-        if (t < 2) sm.ctr[t] = 0u;
-        __syncthreads();
-        // ---- refine (a7) --------------------------------------------------
-        if (in_lds && need == m) {
-          for (uint32_t i = t; i < m; i += BLOCK) out[cr.above + i] = sm.u.c.idx[i];
-        } else if (in_lds && m <= (uint32_t)kRankMax) {
-          rank_select<BLOCK>(sm.u.c.key, sm.u.c.idx, m, need, out, cr.above);
-        } else if (in_lds) {
+        if (m <= (uint32_t)kRankMax) {
+          rank_select<BLOCK>(sm.u.c.key, sm.u.c.idx, m, need, out, above);
+        } else {
           const RSel s = radix_select<BLOCK>(
               [&](auto&& f) {
                 for (uint32_t i = t; i < m; i += BLOCK) f(sm.u.c.key[i]);
               },
-              need, sm.dh, &sm.cross, sm.scan, nullptr, nullptr, 1, nullptr);
+              need, sm.dh, &sm.cross, sm.scan, nullptr, nullptr, 1, nbar, nullptr);
           emit_list(
               [&](auto&& f) {
                 for (uint32_t i = t; i < m; i += BLOCK) f(sm.u.c.key[i], sm.u.c.idx[i]);
               },
-              s, out, cr.above, cr.above + (need - s.rem), (uint32_t)K, sm.ctr);
-        } else {
-          // the crossing bin's members, picked out of the list by their bin
-          const int bs = cr.b;
-          auto members = [&](auto&& f) {
-            for (uint32_t i = t; i < total; i += BLOCK) {
-              const uint2 pr = s_pair[i];
-              if (vbin(from_key(pr.x), gmin, sc) == bs) f(pr.x, (int32_t)pr.y);
-            }
-          };
-          const RSel s = radix_select<BLOCK>(
-              [&](auto&& f) { members([&](uint32_t key, int32_t) { f(key); }); }, need, sm.dh,
-              &sm.cross, sm.scan, nullptr, nullptr, 1, nullptr);
-          emit_list(members, s, out, cr.above, cr.above + (need - s.rem), (uint32_t)K, sm.ctr);
+              s, out, above, above + (need - s.rem), (uint32_t)K, sm.ctr);
         }
-        rest_slot(sf, t, BLOCK);
-        put_stats(1, (int)cr.m, (int)cr.above, cr.b);
-        return;
       }
-      // The list missed the sample's prediction (fewer than K scores above
-      // the floor, or more than it holds): the row's workgroups, whose parts
-      // are still resident, take the parallel rescue together.
-      path = 4;
+      rest_slot(sf, t, BLOCK);
+      put_stats(1, (int)cr.m, (int)cr.above, cr.b);
+      return;
     }
   }
 
   // ---- rescue (a8): exact radix select over the whole row -----------------
   {
     const RSel s = radix_select<BLOCK, true>(resident, (uint32_t)K, sm.dh, &sm.cross, sm.scan,
-                                       SPLIT ? &sf->dig[0][0] : nullptr, hdr, G, err);
+                                             SPLIT ? &sf->dig[0][0] : nullptr, hdr, G, nbar, err);
     uint32_t ngt = 0, neq = 0;
     each([&](int j, int q, bool) {
 #pragma unroll

@@ -63,6 +63,9 @@ int make_plan(int32_t num_rows, int64_t env_len, int32_t k, int32_t force_g, int
   } else if (single >= 0 &&
              (int64_t)num_rows * (kSingleVariants[single].block / 256) >= kFillUnits) {
     G = 1;  // enough rows to fill the chip with whole rows
+  } else if (single == 0) {
+    G = 1;  // rows short enough for the smallest workgroup: splitting costs more
+            // in cross-workgroup latency than it gains in bandwidth
   } else {
     const int64_t part_max = (int64_t)kSplitBlock * kSplitQpt[2];
     const int64_t g_min = (Qmax + part_max - 1) / part_max;
@@ -111,8 +114,8 @@ int make_plan(int32_t num_rows, int64_t env_len, int32_t k, int32_t force_g, int
       p.xcd_group = 0;
       slots = rpl;
     }
-    p.ws_bytes = ws_bytes_for((int)slots);
-    p.cap = kSplitCapMax;
+    p.ws_bytes = ws_bytes_for((int)slots, G);
+    p.cap = kSingleCap;
   }
   *pl = p;
   return TOPK_OK;
@@ -127,7 +130,7 @@ size_t ws_bytes_upper(int32_t num_rows, int64_t env_len, int32_t k, int32_t forc
   int64_t rpl = num_rows < kMaxSlots ? num_rows : kMaxSlots;
   int64_t slots = ((rpl + 7) / 8) * 8;
   if (slots > kMaxSlots) slots = kMaxSlots;
-  return ws_bytes_for((int)slots);
+  return ws_bytes_for((int)slots, p.G);
 }
 
 int validate(int mode, const void* logits, int64_t row_stride, const void* e1, const void* e2,
@@ -391,6 +394,17 @@ int topk_device_query(int64_t* out) {
       out[19 + ki * 3 + qi] = d->regs[ki][qi];
       out[28 + ki * 3 + qi] = d->lds[ki][qi];
     }
+  return TOPK_OK;
+}
+
+int topk_workspace_layout(int64_t* out) {
+  if (!out) return TOPK_EINVAL;
+  out[0] = (int64_t)kWsHeaderBytes;
+  out[1] = (int64_t)sizeof(SlotFixed);
+  out[2] = kMaxSlots;
+  out[3] = (int64_t)kWsDataOff;
+  out[4] = (int64_t)kSliceBytes;
+  out[5] = (int64_t)kListBytes;
   return TOPK_OK;
 }
 

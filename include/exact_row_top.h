@@ -165,6 +165,14 @@ int topk_plan_query(int32_t num_rows, int64_t row_stride, int64_t max_row_len, i
  * Returns a status. */
 int topk_device_query(int64_t* out);
 
+/* Workspace layout (host-only): out[0] = error header bytes, out[1] = bytes
+ * of each slot's fixed block (header, rescue digit counts, row histogram:
+ * every word rests at zero between calls), out[2] = slots, out[3] = byte
+ * offset of the per-slot data blocks; a plan with G workgroups per row has
+ * data blocks of G * out[4] + out[5] bytes (out[4] = one workgroup's slice of
+ * suffix counts, out[5] = the crossing-bin member list).  Returns a status. */
+int topk_workspace_layout(int64_t* out);
+
 /* Host-side argument validation exactly as the entry points run it (no device
  * access).  mode: 0 decode (extents = n_valid, extents2 unused), 1 prefill. */
 int topk_validate(int32_t mode, const void* logits, int64_t row_stride, const void* extents,

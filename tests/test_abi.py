@@ -93,6 +93,18 @@ def test_validate_workspace_size():
     assert _validate(stride=131072, rows=64, k=2048, ws=P16, ws_bytes=need - 1) == ert.TOPK_EWORKSPACE
 
 
+def test_workspace_layout():
+    lay = ert.workspace_layout()
+    assert lay["header_bytes"] == 256 and lay["slots"] == 256
+    assert lay["slot_fixed_bytes"] % 256 == 0
+    assert lay["data_offset"] == lay["header_bytes"] + lay["slots"] * lay["slot_fixed_bytes"]
+    assert lay["slice_bytes"] == 4 * 2048       # one suffix count per bin
+    assert lay["list_bytes"] >= 8 * 2048        # the crossing bin's members, (key, index)
+    p = ert.plan_query(64, 131072, 2048)
+    per_slot = p["wgs_per_row"] * lay["slice_bytes"] + lay["list_bytes"]
+    assert ert.workspace_bytes(64, 131072, 2048) >= lay["data_offset"] + 64 * per_slot
+
+
 def test_workspace_bytes():
     assert ert.workspace_bytes(4096, 16640, 1024) == 0      # one workgroup per row
     assert ert.workspace_bytes(0, 4096, 512) == 0
@@ -112,7 +124,7 @@ def test_plans_for_the_workloads():
         p = ert.plan_query(rows, stride, k)
         assert p["wgs_per_row"] > 1 and p["block"] == 256
         assert p["wgs_per_row"] * p["quads_per_thread"] * 256 >= (stride + 6) // 4
-        assert p["cap"] == 16384
+        assert p["cap"] == 2048
     # capacity bounds rows per launch (co-resident split workgroups)
     p = ert.plan_query(64, 131072, 2048, cu_count=16, wgs_per_cu=2)
     assert p["rows_per_launch"] * p["wgs_per_row"] <= 32 and p["launches"] > 1

@@ -64,9 +64,9 @@ def test_tie_heavy_paths(ert):
     assert st[r6, 0] == 3                                   # 40K in the crossing region -> rescue
     assert st[r6, 1] == -1 or st[r6, 1] > st[r6, 7]
     log(f"[paths] {dict(zip(kinds, st[:, 0].tolist()))}")
-    # sorted rows defeat the floor estimate (the sample's blocks are runs of
-    # equal values): the list misses and the parallel rescue finishes the row
-    assert st[kinds.index("quantised64_sorted"), 0] in (3, 4)
+    # sorted rows can defeat the sample's floor estimate (its blocks are runs
+    # of equal values); whichever exact path finishes the row, parity holds
+    assert st[kinds.index("quantised64_sorted"), 0] in (1, 3, 4)
 
 
 # ---- tiers must agree ------------------------------------------------------------
@@ -201,12 +201,13 @@ def test_caller_workspace_matches_and_returns_to_rest(ert):
         assert_parity(w, got, want)
     torch.cuda.synchronize()
     words = ws.view(torch.int32).cpu().numpy()
-    assert np.all(words[:64] == 0)                      # no error flags
-    # one 64-word header per slot after the 64-word error area: word 1 is the
-    # barrier generation (keeps counting), every other word rests at zero
-    hdrs = words[64:64 + 256 * 64].reshape(256, 64)
-    assert np.all(hdrs[:, 0] == 0) and np.all(hdrs[:, 2:] == 0), "slot headers not at rest"
-    assert np.any(hdrs[:w.num_rows, 1] != 0)             # the barriers did run
+    lay = ert.workspace_layout()
+    h, f, n = lay["header_bytes"] // 4, lay["slot_fixed_bytes"] // 4, lay["slots"]
+    assert np.all(words[:h] == 0)                       # no error flags
+    # one fixed block per slot after the error header: every word (barrier
+    # counter, cursors, digit counts, row histogram) rests at zero
+    blocks = words[h:h + n * f].reshape(n, f)
+    assert np.all(blocks == 0), "slot blocks not at rest"
 
 
 def test_repeat_runs_are_stable(ert):
