@@ -28,7 +28,10 @@ struct Variant {
   int qpt;
 };
 // One workgroup per row; resident capacity block * qpt * 4 scores.
-constexpr Variant kSingleVariants[] = {{256, 8}, {512, 9}, {1024, 9}};
+// In order of capacity; the planner takes the first that holds the row.  Few
+// waves per row keep the per-row fixed work (sample, scans, crossing, edges,
+// refine) small next to the per-score work.
+constexpr Variant kSingleVariants[] = {{256, 8}, {256, 17}, {512, 9}, {1024, 9}};
 // G workgroups per row, each holding 1/G of the row.
 constexpr int kSplitBlock = 256;
 constexpr int kSplitQpt[] = {4, 8, 17};

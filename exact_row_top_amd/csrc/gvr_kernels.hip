@@ -355,15 +355,15 @@ __device__ __forceinline__ float bin_edge(int b, const BinMap& bm) {
     if (mask != 0ull && (mask & 1ull) == 0ull) {
       // the first passing lane is the edge unless probes were clamped
       const int f = __ffsll((unsigned long long)mask) - 1;
-      const uint32_t e = __shfl(probe, f, 64);
-      const uint32_t below = __shfl(probe, f - 1, 64);
+      const uint32_t e = (uint32_t)__builtin_amdgcn_readlane((int)probe, f);
+      const uint32_t below = (uint32_t)__builtin_amdgcn_readlane((int)probe, f - 1);
       if (below + 1u == e) return from_key(e);
       lo = below;
       hi = e;
     } else if (mask == 0ull) {
-      lo = __shfl(probe, 63, 64);
+      lo = (uint32_t)__builtin_amdgcn_readlane((int)probe, 63);
     } else {
-      hi = __shfl(probe, 0, 64);
+      hi = (uint32_t)__builtin_amdgcn_readlane((int)probe, 0);
     }
   }
   while (hi - lo > 1u) {
@@ -374,8 +374,8 @@ __device__ __forceinline__ float bin_edge(int b, const BinMap& bm) {
     const bool ok = vbin(from_key(probe), bm) >= b;
     const uint64_t mask = __ballot(ok);  // lane 63 probes hi, so mask != 0
     const int f = __ffsll((unsigned long long)mask) - 1;
-    const uint32_t nhi = __shfl(probe, f, 64);
-    const uint32_t nlo = (f > 0) ? __shfl(probe, f - 1, 64) : lo;
+    const uint32_t nhi = (uint32_t)__builtin_amdgcn_readlane((int)probe, f);
+    const uint32_t nlo = (f > 0) ? (uint32_t)__builtin_amdgcn_readlane((int)probe, f - 1) : lo;
     lo = nlo;
     hi = nhi;
   }
@@ -534,18 +534,20 @@ struct alignas(16) Smem {
   uint32_t ctr[4];
 };
 
-// Occupancy the one-workgroup variants of up to 512 threads are compiled for
-// (K <= 1024 for 512 threads): eight waves per SIMD (64 VGPRs), so that four
-// 512-thread workgroups share a compute unit.  The others keep the
-// compiler's choice (at 64 VGPRs they would spill).
-template <int K, int BLOCK, bool SPLIT>
+// Occupancy the one-workgroup variants with up to 9 groups per thread and up
+// to 512 threads are compiled for (K <= 1024 for 512 threads): eight waves
+// per SIMD (64 VGPRs), so that four 512-thread workgroups share a compute
+// unit.  The others keep the compiler's choice (at 64 VGPRs they would
+// spill).
+template <int K, int QPT, int BLOCK, bool SPLIT>
 struct WavesPerEu {
-  static constexpr int value = (SPLIT || BLOCK > 512 || (BLOCK == 512 && K > 1024)) ? 1 : 8;
+  static constexpr int value =
+      (SPLIT || QPT > 9 || BLOCK > 512 || (BLOCK == 512 && K > 1024)) ? 1 : 8;
 };
 
 template <int K, int QPT, int BLOCK, bool SPLIT>
 __global__ void __launch_bounds__(BLOCK)
-    __attribute__((amdgpu_waves_per_eu(WavesPerEu<K, BLOCK, SPLIT>::value)))
+    __attribute__((amdgpu_waves_per_eu(WavesPerEu<K, QPT, BLOCK, SPLIT>::value)))
     gvr_topk_kernel(const GvrParams p) {
   constexpr int W = BLOCK / 64;           // waves
   constexpr int NSB = K / 64;             // sample blocks
@@ -662,6 +664,8 @@ __global__ void __launch_bounds__(BLOCK)
   f4 v[QPT];
 #pragma unroll
   for (int j = 0; j < QPT; ++j) {
+    // wave-uniform branches: whole waves inside or outside the part take no
+    // per-lane select
     const int q = q0 + t + j * BLOCK;
     if (q < q1) {
       v[j] = __builtin_nontemporal_load(base + q);
@@ -745,15 +749,19 @@ __global__ void __launch_bounds__(BLOCK)
     const int qlast = Q - 1;
     const int tail = span - (qlast << 2);  // valid lanes in the last group, 1..4
     if (tail < 4 && qlast >= q0 && qlast < q1) {
+      // group jl (uniform) of thread tl holds it: only that thread's wave
+      // takes the branch, and only group jl's registers are touched
       const int d = qlast - q0;
-      if ((d % BLOCK) == t) {
-        const int jl = d / BLOCK;
+      const int jl = d / BLOCK;
+      const int tl = d - jl * BLOCK;
+      if (w == (tl >> 6)) {
+        const bool mine = l == (tl & 63);
 #pragma unroll
         for (int j = 0; j < QPT; ++j)
           if (j == jl) {
 #pragma unroll
             for (int e = 1; e < 4; ++e)
-              if (e >= tail) v[j][e] = qnan;
+              if (e >= tail) v[j][e] = mine ? qnan : v[j][e];
           }
       }
     }
@@ -813,15 +821,17 @@ __global__ void __launch_bounds__(BLOCK)
       {
         const float xlo = sm.thr[0], xhi = sm.thr[1];
         each([&](int j, int q, bool) {
+          // one nibble per mask and group (inline bit constants), shifted in
+          uint32_t nw = 0u, ng = 0u;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int i = j * 4 + e;
             const float x = v[j][e];
-            const bool win = x >= xhi;
-            const bool cand = (x >= xlo) && !win;
-            wb[i >> 5] |= win ? (1u << (i & 31)) : 0u;
-            cb[i >> 5] |= cand ? (1u << (i & 31)) : 0u;
+            nw |= (x >= xhi) ? (1u << e) : 0u;
+            ng |= (x >= xlo) ? (1u << e) : 0u;
           }
+          const int sh = (j * 4) & 31;
+          wb[(j * 4) >> 5] |= nw << sh;
+          cb[(j * 4) >> 5] |= (ng & ~nw) << sh;
         });
       }
       uint32_t nwin = 0, ncand = 0;
@@ -1041,15 +1051,17 @@ __global__ void __launch_bounds__(BLOCK)
       {
         const float xlo = sm.thr[0], xhi = sm.thr[1];
         each([&](int j, int q, bool) {
+          // one nibble per mask and group (inline bit constants), shifted in
+          uint32_t nw = 0u, ng = 0u;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int i = j * 4 + e;
             const float x = v[j][e];
-            const bool win = x >= xhi;
-            const bool cand = (x >= xlo) && !win;
-            wb[i >> 5] |= win ? (1u << (i & 31)) : 0u;
-            cb[i >> 5] |= cand ? (1u << (i & 31)) : 0u;
+            nw |= (x >= xhi) ? (1u << e) : 0u;
+            ng |= (x >= xlo) ? (1u << e) : 0u;
           }
+          const int sh = (j * 4) & 31;
+          wb[(j * 4) >> 5] |= nw << sh;
+          cb[(j * 4) >> 5] |= (ng & ~nw) << sh;
         });
       }
       uint32_t nwin = 0, ncand = 0;
@@ -1217,6 +1229,7 @@ static const void* pick(int block, int qpt, bool split) {
     }
   }
   if (block == 256 && qpt == 8) return kernel_ptr<K, 8, 256, false>();
+  if (block == 256 && qpt == 17) return kernel_ptr<K, 17, 256, false>();
   if (block == 512 && qpt == 9) return kernel_ptr<K, 9, 512, false>();
   if (block == 1024 && qpt == 9) return kernel_ptr<K, 9, 1024, false>();
   return nullptr;
