@@ -69,6 +69,40 @@ def test_tie_heavy_paths(ert):
     assert st[kinds.index("quantised64_sorted"), 0] in (1, 3, 4)
 
 
+def _sample_block_starts(nv, k):
+    # the block64 sample placement read from the pages (K/64 blocks of 64
+    # scores spread over the valid window, both ends included)
+    nsb = k // 64
+    return [(j * (nv - 64)) // (nsb - 1) for j in range(nsb)]
+
+
+@pytest.mark.parametrize("k", [512, 2048])
+def test_sample_seeking_rows_take_the_rescue(ert, k):
+    # Rows whose K largest scores sit exactly on the sample's blocks: the
+    # sample then over-represents the top, the floor taken from it lies above
+    # the K-th value, the merged counts miss K, and the split tier must finish
+    # the row with the parallel rescue.  The answer is unique (index-exact).
+    rows, stride = 4, 65536
+    nv = [60000, 59999, 60000, 40000]
+    w = workloads.random_decode(rows, stride, nv, k, seed=77, dist="normal")
+    for r in (0, 1):
+        pos = [s + i for s in _sample_block_starts(nv[r], k) for i in range(64)]
+        assert len(set(pos)) == k
+        w.logits[r, pos] = (100.0 + 0.001 * np.arange(k)).astype(np.float32)
+    want = oracle.topk_workload(w)
+    for r in (0, 1):
+        assert sorted(want[r].tolist()) == sorted(pos if r == 1 else
+                                                  [s + i for s in _sample_block_starts(nv[0], k)
+                                                   for i in range(64)])
+    for kw in ({}, {"force_wgs_per_row": 4}):
+        log(f"[sample-seeking] k={k} {kw}")
+        got, st = run_gpu(w, stats=True, **kw)
+        assert_parity(w, got, want)
+        for r in (0, 1):
+            assert st[r, 6] > 1 and st[r, 0] == 4, st[r]
+            assert sorted(got[r].tolist()) == sorted(want[r].tolist())
+
+
 # ---- tiers must agree ------------------------------------------------------------
 
 @pytest.mark.parametrize("k", [512, 1024, 2048])
