@@ -34,7 +34,13 @@ class TopKError(RuntimeError):
 class _Options(ctypes.Structure):
     _fields_ = [("force_wgs_per_row", ctypes.c_int32),
                 ("force_rescue", ctypes.c_int32),
-                ("row_stats", ctypes.c_void_p)]
+                ("row_stats", ctypes.c_void_p),
+                ("values", ctypes.c_void_p),
+                ("flags", ctypes.c_uint32)]
+
+
+TOPK_SORTED = 1
+TOPK_DETERMINISTIC = 2
 
 
 def load_library():
@@ -50,6 +56,10 @@ def load_library():
     lib.topk_decode.restype = ctypes.c_int
     lib.topk_prefill.argtypes = [P, I64, P, P, I32, I32, P, I64, P, SZ, P]
     lib.topk_prefill.restype = ctypes.c_int
+    lib.topk_decode_v.argtypes = [P, I64, P, I32, I32, P, P, ctypes.c_uint32, P, SZ, P]
+    lib.topk_decode_v.restype = ctypes.c_int
+    lib.topk_prefill_v.argtypes = [P, I64, P, P, I32, I32, P, P, ctypes.c_uint32, I64, P, SZ, P]
+    lib.topk_prefill_v.restype = ctypes.c_int
     lib.topk_decode_ex.argtypes = [P, I64, P, I32, I32, P, P, SZ, P, ctypes.POINTER(_Options)]
     lib.topk_decode_ex.restype = ctypes.c_int
     lib.topk_prefill_ex.argtypes = [P, I64, P, P, I32, I32, P, I64, P, SZ, P,
@@ -170,7 +180,7 @@ def _out(indices, rows, k, device):
     return indices
 
 
-def _opts(force_wgs_per_row, force_rescue, row_stats, rows):
+def _opts(force_wgs_per_row, force_rescue, row_stats, rows, values=None, flags=0):
     import torch
     if not (force_wgs_per_row or force_rescue or row_stats is not None):
         return None
@@ -179,8 +189,26 @@ def _opts(force_wgs_per_row, force_rescue, row_stats, rows):
         if tuple(row_stats.shape) != (rows, STATS_WORDS) or not row_stats.is_contiguous():
             raise ValueError(f"row_stats must be a contiguous int32 [{rows}, {STATS_WORDS}] tensor")
     o = _Options(int(force_wgs_per_row), int(bool(force_rescue)),
-                 row_stats.data_ptr() if row_stats is not None else None)
+                 row_stats.data_ptr() if row_stats is not None else None,
+                 values.data_ptr() if values is not None else None, int(flags))
     return ctypes.pointer(o)
+
+
+def _values(values, return_values, rows, k, device):
+    """The values output tensor (float32 [rows, k]) or None."""
+    import torch
+    if values is None:
+        if not return_values:
+            return None
+        return torch.empty((rows, k), dtype=torch.float32, device=device)
+    _require(values, "values", torch.float32, 2)
+    if tuple(values.shape) != (rows, k) or not values.is_contiguous() or values.device != device:
+        raise ValueError(f"values must be a contiguous float32 [{rows}, {k}] tensor on {device}")
+    return values
+
+
+def _flags(sorted_, deterministic):
+    return (TOPK_SORTED if sorted_ else 0) | (TOPK_DETERMINISTIC if deterministic else 0)
 
 
 def _ws(workspace):
@@ -190,8 +218,15 @@ def _ws(workspace):
 
 
 def topk_decode(logits, n_valid, k: int, indices=None, *, workspace=None, stream=None,
-                force_wgs_per_row: int = 0, force_rescue: bool = False, row_stats=None):
-    """Exact top-k of logits[r, :n_valid[r]] per row (local indices, -1 pad)."""
+                values=None, return_values: bool = False, sorted: bool = False,
+                deterministic: bool = False, force_wgs_per_row: int = 0,
+                force_rescue: bool = False, row_stats=None):
+    """Exact top-k of logits[r, :n_valid[r]] per row (local indices, -1 pad).
+
+    values / return_values: also the selected scores (-FLT_MAX pad); sorted:
+    long rows ordered by value descending, then index ascending;
+    deterministic: the k-th value's ties resolved by smallest index.  Returns
+    the indices, or (indices, values) when values are asked for."""
     import torch
     lib = load_library()
     rows, row_stride = _logits_layout(logits)
@@ -199,23 +234,32 @@ def topk_decode(logits, n_valid, k: int, indices=None, *, workspace=None, stream
     if n_valid.shape[0] != rows or not n_valid.is_contiguous():
         raise ValueError("n_valid must be a contiguous int32 [rows] tensor")
     out = _out(indices, rows, k, logits.device)
+    vals = _values(values, return_values, rows, k, logits.device)
+    flags = _flags(sorted, deterministic)
     wp, wb = _ws(workspace)
-    opts = _opts(force_wgs_per_row, force_rescue, row_stats, rows)
+    opts = _opts(force_wgs_per_row, force_rescue, row_stats, rows, vals, flags)
     s = _stream_ptr(stream, logits.device)
-    if opts is None:
-        rc = lib.topk_decode(logits.data_ptr(), row_stride, n_valid.data_ptr(), rows, k,
-                             out.data_ptr(), wp, wb, s)
-    else:
+    if opts is not None:
         rc = lib.topk_decode_ex(logits.data_ptr(), row_stride, n_valid.data_ptr(), rows, k,
                                 out.data_ptr(), wp, wb, s, opts)
+    elif vals is not None or flags:
+        rc = lib.topk_decode_v(logits.data_ptr(), row_stride, n_valid.data_ptr(), rows, k,
+                               out.data_ptr(), vals.data_ptr() if vals is not None else None,
+                               flags, wp, wb, s)
+    else:
+        rc = lib.topk_decode(logits.data_ptr(), row_stride, n_valid.data_ptr(), rows, k,
+                             out.data_ptr(), wp, wb, s)
     _check(rc)
-    return out
+    return (out, vals) if vals is not None else out
 
 
 def topk_prefill(logits, row_starts, row_ends, k: int, indices=None, *, max_row_len: int = 0,
-                 workspace=None, stream=None, force_wgs_per_row: int = 0,
+                 workspace=None, stream=None, values=None, return_values: bool = False,
+                 sorted: bool = False, deterministic: bool = False, force_wgs_per_row: int = 0,
                  force_rescue: bool = False, row_stats=None):
-    """Exact top-k of logits[r, row_starts[r]:row_ends[r]] per row (ks-relative)."""
+    """Exact top-k of logits[r, row_starts[r]:row_ends[r]] per row (ks-relative).
+
+    Output options as for topk_decode."""
     import torch
     lib = load_library()
     rows, row_stride = _logits_layout(logits)
@@ -224,19 +268,26 @@ def topk_prefill(logits, row_starts, row_ends, k: int, indices=None, *, max_row_
         if t.shape[0] != rows or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous int32 [rows] tensor")
     out = _out(indices, rows, k, logits.device)
+    vals = _values(values, return_values, rows, k, logits.device)
+    flags = _flags(sorted, deterministic)
     wp, wb = _ws(workspace)
-    opts = _opts(force_wgs_per_row, force_rescue, row_stats, rows)
+    opts = _opts(force_wgs_per_row, force_rescue, row_stats, rows, vals, flags)
     s = _stream_ptr(stream, logits.device)
-    if opts is None:
-        rc = lib.topk_prefill(logits.data_ptr(), row_stride, row_starts.data_ptr(),
-                              row_ends.data_ptr(), rows, k, out.data_ptr(), int(max_row_len),
-                              wp, wb, s)
-    else:
+    if opts is not None:
         rc = lib.topk_prefill_ex(logits.data_ptr(), row_stride, row_starts.data_ptr(),
                                  row_ends.data_ptr(), rows, k, out.data_ptr(), int(max_row_len),
                                  wp, wb, s, opts)
+    elif vals is not None or flags:
+        rc = lib.topk_prefill_v(logits.data_ptr(), row_stride, row_starts.data_ptr(),
+                                row_ends.data_ptr(), rows, k, out.data_ptr(),
+                                vals.data_ptr() if vals is not None else None, flags,
+                                int(max_row_len), wp, wb, s)
+    else:
+        rc = lib.topk_prefill(logits.data_ptr(), row_stride, row_starts.data_ptr(),
+                              row_ends.data_ptr(), rows, k, out.data_ptr(), int(max_row_len),
+                              wp, wb, s)
     _check(rc)
-    return out
+    return (out, vals) if vals is not None else out
 
 
 def new_workspace(num_rows: int, row_stride: int, k: int, device="cuda", stream=None):
@@ -251,4 +302,5 @@ def new_workspace(num_rows: int, row_stride: int, k: int, device="cuda", stream=
 
 
 __all__ = ["topk_decode", "topk_prefill", "workspace_bytes", "new_workspace", "plan_query",
-           "strerror", "load_library", "TopKError", "STATS_WORDS", "VALID_K"]
+           "strerror", "load_library", "TopKError", "STATS_WORDS", "VALID_K", "TOPK_SORTED",
+           "TOPK_DETERMINISTIC"]

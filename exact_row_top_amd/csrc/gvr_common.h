@@ -42,7 +42,7 @@ constexpr int kStatsWords = 8;
 
 // Workspace layout (bytes):
 //   [0, 256)                             error flags (word 0)
-//   kMaxSlots fixed blocks of 12544 bytes: SlotHeader, digit counts [4][256],
+//   kMaxSlots fixed blocks of 16640 bytes: SlotHeader, digit counts [8][256],
 //   value histogram [kBins]
 //   then one data block per slot: G slices of kBins suffix counts (slice g:
 //   workgroup g's count of scores in bins >= b), then the crossing bin's
@@ -63,10 +63,11 @@ static_assert(sizeof(SlotHeader) == 256, "slot header size");
 
 struct SlotFixed {
   SlotHeader hdr;
-  uint32_t dig[4][256];  // rescue digit counts, one row per radix level
+  uint32_t dig[8][256];  // rescue digit counts, one row per radix level
+                         // (rows 4..7: the deterministic tie pick)
   uint32_t hist[2048];   // the row's value histogram (bins >= the floor bin)
 };
-static_assert(sizeof(SlotFixed) == 12544, "slot fixed block size");
+static_assert(sizeof(SlotFixed) == 16640, "slot fixed block size");
 
 constexpr size_t kWsHeaderBytes = 256;
 constexpr size_t kWsDataOff = kWsHeaderBytes + sizeof(SlotFixed) * kMaxSlots;
@@ -94,9 +95,25 @@ struct GvrParams {
   int32_t xcd_group;  // 1: map a row's workgroups onto one XCD
   int32_t cap;        // candidate cap of this plan
   int32_t force_rescue;
+  int32_t deterministic;  // resolve the K-th value's tie class by smallest index
   int32_t* indices;
   int32_t* row_stats;  // optional
   unsigned char* ws;   // workspace base (split tier), or nullptr
+};
+
+// Output epilogue (values, sorting): one workgroup per row.
+constexpr int kEpiBlock = 256;
+
+struct EpiParams {
+  const float* logits;
+  int64_t row_stride;
+  const int32_t* n_valid;     // decode form, or nullptr
+  const int32_t* row_starts;  // prefill form
+  const int32_t* row_ends;
+  int32_t row_begin;
+  int32_t sorted;
+  int32_t* indices;
+  float* values;  // optional
 };
 
 }  // namespace ert

@@ -423,7 +423,7 @@ __device__ __forceinline__ bool finish_slot(SlotHeader* hdr, int G, uint32_t* bc
 }
 
 __device__ __forceinline__ void rest_slot(SlotFixed* sf, int t, int block) {
-  for (int i = t; i < 4 * 256; i += block) (&sf->dig[0][0])[i] = 0u;
+  for (int i = t; i < 8 * 256; i += block) (&sf->dig[0][0])[i] = 0u;
   for (int i = t; i < kBins; i += block) sf->hist[i] = 0u;
   if (t == 0) {
     sf->hdr.bar_count = 0u;
@@ -442,6 +442,7 @@ struct RSel {
   uint32_t thr;    // key >> shift of the threshold digit path
   int shift;       // 24, 16, 8 or 0
   uint32_t rem;    // how many of the elements with key >> shift == thr to take
+  uint32_t cnt;    // how many elements have key >> shift == thr
 };
 
 // The `need` largest keys among the elements `iter` visits (iter(f) calls
@@ -456,7 +457,7 @@ __device__ __forceinline__ RSel radix_select(Iter&& iter, uint32_t need, uint32_
                                              uint32_t* scan, uint32_t* gdig, SlotHeader* hdr, int G,
                                              uint32_t& nbar, uint32_t* err) {
   const int t = threadIdx.x;
-  uint32_t prefix = 0, rem = need;
+  uint32_t prefix = 0, rem = need, cnt = 0;
   int shift = 24;
   for (int L = 0; L < 4; ++L) {
     shift = 24 - 8 * L;
@@ -484,29 +485,52 @@ __device__ __forceinline__ RSel radix_select(Iter&& iter, uint32_t need, uint32_
     const Cross c = *cross;
     prefix |= (uint32_t)c.b << shift;
     rem -= c.above;
+    cnt = c.m;
     if (c.m == rem) break;
   }
-  return RSel{prefix >> shift, shift, rem};
+  return RSel{prefix >> shift, shift, rem, cnt};
 }
 
-// Write the selected elements of a list (iter2(f) calls f(key, index) for
-// this thread's elements): those above the threshold digit take consecutive
-// slots from out[gt_base], the first `rem` equal ones (by ticket) from
-// out[eq_base].  `ctr` is two LDS words, zero on entry.
-template <class Iter2>
-__device__ __forceinline__ void emit_list(Iter2&& iter2, const RSel& s, int32_t* out,
-                                          uint32_t gt_base, uint32_t eq_base, uint32_t limit,
-                                          uint32_t* ctr) {
-  iter2([&](uint32_t key, int32_t idx) {
-    const uint32_t d = key >> s.shift;
+// The `need` largest of the m (key, index) pairs held in LDS, written from
+// out[base] on (those in the K-th key's digit class after the others): an
+// 8-bit radix select over the keys.  With `det`, when the K-th key's class
+// holds more members than are needed, a second radix select over the
+// complemented indices of that class (non-members count as key 0) keeps the
+// smallest indices: that class then always ends with every member of its last
+// digit needed, so the choice involves no ticket.  `ctr` is two LDS words,
+// zero on entry.
+template <int BLOCK>
+__device__ __forceinline__ void list_select(const uint32_t* key, const int32_t* idx, uint32_t m,
+                                            uint32_t need, bool det, int32_t* out, uint32_t base,
+                                            uint32_t limit, uint32_t* dh, Cross* cross,
+                                            uint32_t* scan, uint32_t* ctr, uint32_t& nbar) {
+  const int t = threadIdx.x;
+  const RSel s = radix_select<BLOCK>(
+      [&](auto&& f) {
+        for (uint32_t i = t; i < m; i += BLOCK) f(key[i]);
+      },
+      need, dh, cross, scan, nullptr, nullptr, 1, nbar, nullptr);
+  const bool pick = det && s.cnt > s.rem;
+  RSel s2{0u, 0, 0u, 0u};
+  if (pick) {
+    const uint32_t tk = s.thr;  // the loop ran all four levels: one exact key
+    s2 = radix_select<BLOCK>(
+        [&](auto&& f) {
+          for (uint32_t i = t; i < m; i += BLOCK) f(key[i] == tk ? ~(uint32_t)idx[i] : 0u);
+        },
+        s.rem, dh, cross, scan, nullptr, nullptr, 1, nbar, nullptr);
+  }
+  const uint32_t eq_base = base + (need - s.rem);
+  for (uint32_t i = t; i < m; i += BLOCK) {
+    const uint32_t d = key[i] >> s.shift;
     if (d > s.thr) {
-      const uint32_t pos = gt_base + lds_take(&ctr[0]);
-      if (pos < limit) out[pos] = idx;
-    } else if (d == s.thr) {
+      const uint32_t pos = base + lds_take(&ctr[0]);
+      if (pos < limit) out[pos] = idx[i];
+    } else if (d == s.thr && (!pick || ((~(uint32_t)idx[i]) >> s2.shift) >= s2.thr)) {
       const uint32_t tk = lds_take(&ctr[1]);
-      if (tk < s.rem && eq_base + tk < limit) out[eq_base + tk] = idx;
+      if (tk < s.rem && eq_base + tk < limit) out[eq_base + tk] = idx[i];
     }
-  });
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -885,16 +909,8 @@ __global__ void __launch_bounds__(BLOCK)
       } else if (m <= (uint32_t)kRankMax) {
         rank_select<BLOCK>(sm.u.c.key, sm.u.c.idx, m, need, out, cr.above);
       } else {
-        const RSel s = radix_select<BLOCK>(
-            [&](auto&& f) {
-              for (uint32_t i = t; i < m; i += BLOCK) f(sm.u.c.key[i]);
-            },
-            need, sm.dh, &sm.cross, sm.scan, nullptr, nullptr, 1, nbar, nullptr);
-        emit_list(
-            [&](auto&& f) {
-              for (uint32_t i = t; i < m; i += BLOCK) f(sm.u.c.key[i], sm.u.c.idx[i]);
-            },
-            s, out, cr.above, cr.above + (need - s.rem), (uint32_t)K, sm.ctr);
+        list_select<BLOCK>(sm.u.c.key, sm.u.c.idx, m, need, p.deterministic != 0, out, cr.above,
+                           (uint32_t)K, sm.dh, &sm.cross, sm.scan, sm.ctr, nbar);
       }
       put_stats(1, (int)cr.m, (int)cr.above, cr.b);
       return;
@@ -1134,16 +1150,8 @@ __global__ void __launch_bounds__(BLOCK)
         if (m <= (uint32_t)kRankMax) {
           rank_select<BLOCK>(sm.u.c.key, sm.u.c.idx, m, need, out, above);
         } else {
-          const RSel s = radix_select<BLOCK>(
-              [&](auto&& f) {
-                for (uint32_t i = t; i < m; i += BLOCK) f(sm.u.c.key[i]);
-              },
-              need, sm.dh, &sm.cross, sm.scan, nullptr, nullptr, 1, nbar, nullptr);
-          emit_list(
-              [&](auto&& f) {
-                for (uint32_t i = t; i < m; i += BLOCK) f(sm.u.c.key[i], sm.u.c.idx[i]);
-              },
-              s, out, above, above + (need - s.rem), (uint32_t)K, sm.ctr);
+          list_select<BLOCK>(sm.u.c.key, sm.u.c.idx, m, need, p.deterministic != 0, out, above,
+                             (uint32_t)K, sm.dh, &sm.cross, sm.scan, sm.ctr, nbar);
         }
       }
       rest_slot(sf, t, BLOCK);
@@ -1156,13 +1164,41 @@ __global__ void __launch_bounds__(BLOCK)
   {
     const RSel s = radix_select<BLOCK, true>(resident, (uint32_t)K, sm.dh, &sm.cross, sm.scan,
                                              SPLIT ? &sf->dig[0][0] : nullptr, hdr, G, nbar, err);
+    // Deterministic mode: when the K-th key's class holds more scores than
+    // are needed, keep its smallest positions -- a second radix select over
+    // the class's complemented positions (other scores count as key 0; the
+    // row's workgroups merge through digit rows 4..7).  Positions are
+    // distinct, so that select always ends with its last digit class needed
+    // whole: the choice takes no ticket.
+    const bool pick = p.deterministic && s.cnt > s.rem;
+    RSel s2{0u, 0, 0u, 0u};
+    if (pick) {
+      const uint32_t tkey = s.thr;  // all four levels ran: one exact key
+      s2 = radix_select<BLOCK, true>(
+          [&](auto&& f) {
+            each([&](int j, int q, bool) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                float x = v[j][e];
+                asm volatile("" : "+v"(x));
+                const uint32_t pos = (uint32_t)((q << 2) + e - lead);
+                f(rkey(x) == tkey ? ~pos : 0u);
+              }
+            });
+          },
+          s.rem, sm.dh, &sm.cross, sm.scan, SPLIT ? &sf->dig[4][0] : nullptr, hdr, G, nbar, err);
+    }
+    // a score of the K-th key's class is taken when the tie pick keeps it
+    auto kept = [&](int32_t idx) {
+      return !pick || (((~(uint32_t)idx) >> s2.shift) >= s2.thr);
+    };
     uint32_t ngt = 0, neq = 0;
     each([&](int j, int q, bool) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t d = rkey(v[j][e]) >> s.shift;
         ngt += (d > s.thr) ? 1u : 0u;
-        neq += (d == s.thr) ? 1u : 0u;
+        neq += (d == s.thr && kept((q << 2) + e - lead)) ? 1u : 0u;
       }
     });
     if (t == 0) sm.bc[3] = s.thr;
@@ -1188,9 +1224,9 @@ __global__ void __launch_bounds__(BLOCK)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t d = rkey(v[j][e]) >> s.shift;
-        const bool gt = d > thr2;
-        const bool eq = d == thr2;
         const int32_t idx = (q << 2) + e - lead;
+        const bool gt = d > thr2;
+        const bool eq = d == thr2 && kept(idx);
         if (gt && gpos < (uint32_t)K) out[gpos] = idx;
         if (eq && tk < s.rem) out[eqbase + tk] = idx;
         gpos += gt ? 1u : 0u;

@@ -13,6 +13,7 @@
 
 namespace ert {
 const void* gvr_kernel(int k, int block, int qpt, bool split);
+const void* epilogue_kernel(int k);
 }
 
 using namespace ert;
@@ -219,6 +220,10 @@ int run(int mode, const float* logits, int64_t row_stride, const int32_t* e1, co
   int rc = validate(mode, logits, row_stride, e1, e2, num_rows, k, indices, force_g);
   if (rc != TOPK_OK) return rc;
   if (opts && opts->row_stats && !aligned(opts->row_stats, 4)) return TOPK_ELAYOUT;
+  const uint32_t flags = opts ? opts->flags : 0u;
+  float* values = opts ? opts->values : nullptr;
+  if (flags & ~(uint32_t)(TOPK_SORTED | TOPK_DETERMINISTIC)) return TOPK_EINVAL;
+  if (values && !aligned(values, 4)) return TOPK_ELAYOUT;
   if (num_rows == 0) return TOPK_OK;
   // Plans are sized for the full row stride, so any window inside it fits the
   // resident capacity; the prefill length hint is accepted but not needed.
@@ -279,6 +284,7 @@ int run(int mode, const float* logits, int64_t row_stride, const int32_t* e1, co
   prm.wgs_per_row = pl.G;
   prm.cap = pl.cap;
   prm.force_rescue = (opts && opts->force_rescue) ? 1 : 0;
+  prm.deterministic = (flags & TOPK_DETERMINISTIC) ? 1 : 0;
   prm.indices = indices;
   prm.row_stats = opts ? opts->row_stats : nullptr;
   prm.ws = ws;
@@ -297,6 +303,29 @@ int run(int mode, const float* logits, int64_t row_stride, const int32_t* e1, co
     void* args[] = {&prm};
     if (hipLaunchKernel(kern, dim3((unsigned)grid), dim3(pl.block), args, 0, stream) != hipSuccess)
       return TOPK_ELAUNCH;
+  }
+  if (values || (flags & TOPK_SORTED)) {
+    // output stage: values and / or sorted long rows, one workgroup per row
+    const void* epi = epilogue_kernel(k);
+    if (!epi) return TOPK_EINVAL;
+    EpiParams ep;
+    memset(&ep, 0, sizeof(ep));
+    ep.logits = logits;
+    ep.row_stride = row_stride;
+    ep.n_valid = prm.n_valid;
+    ep.row_starts = prm.row_starts;
+    ep.row_ends = prm.row_ends;
+    ep.sorted = (flags & TOPK_SORTED) ? 1 : 0;
+    ep.indices = indices;
+    ep.values = values;
+    constexpr int64_t kMaxGrid = (int64_t)1 << 30;
+    for (int64_t r0 = 0; r0 < num_rows; r0 += kMaxGrid) {
+      const int64_t nr = (num_rows - r0) < kMaxGrid ? (num_rows - r0) : kMaxGrid;
+      ep.row_begin = (int32_t)r0;
+      void* args[] = {&ep};
+      if (hipLaunchKernel(epi, dim3((unsigned)nr), dim3(kEpiBlock), args, 0, stream) != hipSuccess)
+        return TOPK_ELAUNCH;
+    }
   }
   if (hipGetLastError() != hipSuccess) return TOPK_ELAUNCH;
   return TOPK_OK;
@@ -318,6 +347,29 @@ int topk_prefill(const float* logits, int64_t row_stride, const int32_t* row_sta
                  int64_t max_row_len, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return run(1, logits, row_stride, row_starts, row_ends, num_rows, k, indices, max_row_len,
              workspace, workspace_bytes, stream, nullptr);
+}
+
+int topk_decode_v(const float* logits, int64_t row_stride, const int32_t* n_valid,
+                  int32_t num_rows, int32_t k, int32_t* indices, float* values, uint32_t flags,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  topk_options o;
+  memset(&o, 0, sizeof(o));
+  o.values = values;
+  o.flags = flags;
+  return run(0, logits, row_stride, n_valid, nullptr, num_rows, k, indices, 0, workspace,
+             workspace_bytes, stream, &o);
+}
+
+int topk_prefill_v(const float* logits, int64_t row_stride, const int32_t* row_starts,
+                   const int32_t* row_ends, int32_t num_rows, int32_t k, int32_t* indices,
+                   float* values, uint32_t flags, int64_t max_row_len, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream) {
+  topk_options o;
+  memset(&o, 0, sizeof(o));
+  o.values = values;
+  o.flags = flags;
+  return run(1, logits, row_stride, row_starts, row_ends, num_rows, k, indices, max_row_len,
+             workspace, workspace_bytes, stream, &o);
 }
 
 int topk_decode_ex(const float* logits, int64_t row_stride, const int32_t* n_valid,

@@ -99,6 +99,33 @@ int topk_prefill(const float* logits, int64_t row_stride, const int32_t* row_sta
                  int64_t max_row_len, void* workspace, size_t workspace_bytes,
                  hipStream_t stream);
 
+/* ---- Output options -------------------------------------------------------
+ * Same selection as topk_decode / topk_prefill, with:
+ *  values: optional device float[num_rows][k] (NULL = none), 4-byte aligned.
+ *      values[r][i] is the score at indices[r][i] (logits[r, ks + idx]); short
+ *      rows (nv <= k) keep their identity indices and pad values with
+ *      -FLT_MAX (PR 18122, values-output commit).
+ *  flags: TOPK_SORTED orders each long row's indices (and values) by value
+ *      descending, then index ascending; TOPK_DETERMINISTIC resolves the K-th
+ *      value's tie class by smallest index, so the selected set is the same on
+ *      every call (PR 20998 "What changes" and "Walkthrough": smallest-index
+ *      deterministic ties, optional output sorting).  With both flags a long
+ *      row's output is its canonical top-k: positions ordered by value
+ *      descending, equal values by position ascending.  Short rows are always
+ *      identity + -1.  Unknown flag bits give TOPK_EINVAL.
+ * Values and sorting run as a second kernel on the same stream. */
+#define TOPK_SORTED 1u
+#define TOPK_DETERMINISTIC 2u
+
+int topk_decode_v(const float* logits, int64_t row_stride, const int32_t* n_valid,
+                  int32_t num_rows, int32_t k, int32_t* indices, float* values, uint32_t flags,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+int topk_prefill_v(const float* logits, int64_t row_stride, const int32_t* row_starts,
+                   const int32_t* row_ends, int32_t num_rows, int32_t k, int32_t* indices,
+                   float* values, uint32_t flags, int64_t max_row_len, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream);
+
 /* Bytes of workspace a call with num_rows rows of stride `max_row_len` needs
  * (pass the row_stride of the call; 0 when the plan uses one workgroup per
  * row and needs none).  The value does not depend on the device.  Returns 0
@@ -135,6 +162,8 @@ typedef struct topk_options {
   int32_t force_wgs_per_row;
   int32_t force_rescue;
   int32_t* row_stats;
+  float* values;   /* as in topk_decode_v */
+  uint32_t flags;  /* as in topk_decode_v */
 } topk_options;
 
 int topk_decode_ex(const float* logits, int64_t row_stride, const int32_t* n_valid,
