@@ -60,6 +60,12 @@ def load_library():
     lib.topk_decode_v.restype = ctypes.c_int
     lib.topk_prefill_v.argtypes = [P, I64, P, P, I32, I32, P, P, ctypes.c_uint32, I64, P, SZ, P]
     lib.topk_prefill_v.restype = ctypes.c_int
+    lib.topk_decode_varlen.argtypes = [P, I64, P, I32, I32, I32, I32, P, P, ctypes.c_uint32, P,
+                                       SZ, P]
+    lib.topk_decode_varlen.restype = ctypes.c_int
+    lib.topk_decode_varlen_ex.argtypes = [P, I64, P, I32, I32, I32, I32, P, P, SZ, P,
+                                          ctypes.POINTER(_Options)]
+    lib.topk_decode_varlen_ex.restype = ctypes.c_int
     lib.topk_decode_ex.argtypes = [P, I64, P, I32, I32, P, P, SZ, P, ctypes.POINTER(_Options)]
     lib.topk_decode_ex.restype = ctypes.c_int
     lib.topk_prefill_ex.argtypes = [P, I64, P, P, I32, I32, P, I64, P, SZ, P,
@@ -290,6 +296,42 @@ def topk_prefill(logits, row_starts, row_ends, k: int, indices=None, *, max_row_
     return (out, vals) if vals is not None else out
 
 
+def topk_decode_varlen(logits, kv_lens, k: int, next_n: int = 1, compress_ratio: int = 1,
+                       indices=None, *, workspace=None, stream=None, values=None,
+                       return_values: bool = False, sorted: bool = False,
+                       deterministic: bool = False, force_wgs_per_row: int = 0,
+                       force_rescue: bool = False, row_stats=None):
+    """Exact top-k of the varlen / MTP decode form: row r selects from
+    logits[r, :n] with n = (kv_lens[r // next_n] - next_n + r % next_n + 1) //
+    compress_ratio (no window when kv_lens[r // next_n] < next_n), computed on
+    the device from the per-request kv_lens.  Output options as for
+    topk_decode."""
+    import torch
+    lib = load_library()
+    rows, row_stride = _logits_layout(logits)
+    _require(kv_lens, "kv_lens", torch.int32, 1)
+    need = (rows + int(next_n) - 1) // int(next_n) if next_n >= 1 else 0
+    if not kv_lens.is_contiguous() or kv_lens.shape[0] < need:
+        raise ValueError(f"kv_lens must be a contiguous int32 tensor of >= {need} requests")
+    out = _out(indices, rows, k, logits.device)
+    vals = _values(values, return_values, rows, k, logits.device)
+    flags = _flags(sorted, deterministic)
+    wp, wb = _ws(workspace)
+    opts = _opts(force_wgs_per_row, force_rescue, row_stats, rows, vals, flags)
+    s = _stream_ptr(stream, logits.device)
+    if opts is not None:
+        rc = lib.topk_decode_varlen_ex(logits.data_ptr(), row_stride, kv_lens.data_ptr(), rows,
+                                       int(next_n), int(compress_ratio), k, out.data_ptr(), wp, wb,
+                                       s, opts)
+    else:
+        rc = lib.topk_decode_varlen(logits.data_ptr(), row_stride, kv_lens.data_ptr(), rows,
+                                    int(next_n), int(compress_ratio), k, out.data_ptr(),
+                                    vals.data_ptr() if vals is not None else None, flags, wp, wb,
+                                    s)
+    _check(rc)
+    return (out, vals) if vals is not None else out
+
+
 def new_workspace(num_rows: int, row_stride: int, k: int, device="cuda", stream=None):
     """Allocate and zero a caller-owned workspace (None when the plan needs none)."""
     import torch
@@ -301,6 +343,6 @@ def new_workspace(num_rows: int, row_stride: int, k: int, device="cuda", stream=
     return ws
 
 
-__all__ = ["topk_decode", "topk_prefill", "workspace_bytes", "new_workspace", "plan_query",
+__all__ = ["topk_decode", "topk_prefill", "topk_decode_varlen", "workspace_bytes", "new_workspace", "plan_query",
            "strerror", "load_library", "TopKError", "STATS_WORDS", "VALID_K", "TOPK_SORTED",
            "TOPK_DETERMINISTIC"]

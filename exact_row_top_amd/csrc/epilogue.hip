@@ -13,6 +13,7 @@
 #include <stdint.h>
 
 #include "gvr_common.h"
+#include "row_window.h"
 
 namespace ert {
 
@@ -35,17 +36,7 @@ __global__ void __launch_bounds__(kEpiBlock) topk_epilogue_kernel(const EpiParam
   const int64_t row = (int64_t)p.row_begin + blockIdx.x;
   const int S = (int)p.row_stride;
   int ks, nv;
-  if (p.n_valid) {
-    const int n = p.n_valid[row];
-    ks = 0;
-    nv = n < 0 ? 0 : (n > S ? S : n);
-  } else {
-    int a = p.row_starts[row], e = p.row_ends[row];
-    a = a < 0 ? 0 : (a > S ? S : a);
-    e = e < a ? a : (e > S ? S : e);
-    ks = a;
-    nv = e - a;
-  }
+  row_window(p.n_valid, p.row_starts, p.row_ends, p.varlen, row, S, &ks, &nv);
   int32_t* out = p.indices + row * K;
   float* vals = p.values ? p.values + row * K : nullptr;
   const float* win = p.logits + row * (int64_t)S + ks;

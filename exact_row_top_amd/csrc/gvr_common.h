@@ -83,12 +83,24 @@ constexpr size_t ws_bytes_for(int slots, int G) {
 // Error flags written by the kernel into workspace word 0.
 constexpr uint32_t kErrBarrierTimeout = 1u;
 
+// Varlen / MTP decode form (the heuristic decode contract of PR 18122,
+// run_varlen commit): row r belongs to request r / next_n, whose total cache
+// length is kv_lens[r / next_n]; its window is [0, n) with
+// n = (kv_len - next_n + r % next_n + 1) / compress_ratio, and no window when
+// kv_len < next_n.
+struct VarlenForm {
+  const int32_t* kv_lens;  // per request, or nullptr
+  int32_t next_n;
+  int32_t compress_ratio;
+};
+
 struct GvrParams {
   const float* logits;
   int64_t row_stride;
   const int32_t* n_valid;     // decode form, or nullptr
   const int32_t* row_starts;  // prefill form
   const int32_t* row_ends;
+  VarlenForm varlen;          // varlen decode form (kv_lens != nullptr)
   int32_t row_begin;  // first row handled by this launch
   int32_t rows;       // rows handled by this launch
   int32_t wgs_per_row;
@@ -110,6 +122,7 @@ struct EpiParams {
   const int32_t* n_valid;     // decode form, or nullptr
   const int32_t* row_starts;  // prefill form
   const int32_t* row_ends;
+  VarlenForm varlen;
   int32_t row_begin;
   int32_t sorted;
   int32_t* indices;

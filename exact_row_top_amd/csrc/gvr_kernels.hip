@@ -46,6 +46,7 @@
 #include <stdint.h>
 
 #include "gvr_common.h"
+#include "row_window.h"
 
 namespace ert {
 
@@ -604,17 +605,7 @@ __global__ void __launch_bounds__(BLOCK)
   // ---- row resolve (a0); row_stride < 2^30 is checked on the host --------
   const int S = (int)p.row_stride;
   int ks, nv;
-  if (p.n_valid) {
-    const int n = p.n_valid[row];
-    ks = 0;
-    nv = n < 0 ? 0 : (n > S ? S : n);
-  } else {
-    int a = p.row_starts[row], e = p.row_ends[row];
-    a = a < 0 ? 0 : (a > S ? S : a);
-    e = e < a ? a : (e > S ? S : e);
-    ks = a;
-    nv = e - a;
-  }
+  row_window(p.n_valid, p.row_starts, p.row_ends, p.varlen, row, S, &ks, &nv);
   int32_t* out = p.indices + row * K;
   int32_t* stats = p.row_stats ? p.row_stats + row * kStatsWords : nullptr;
 

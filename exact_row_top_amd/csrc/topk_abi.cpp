@@ -136,7 +136,8 @@ size_t ws_bytes_upper(int32_t num_rows, int64_t env_len, int32_t k, int32_t forc
 
 int validate(int mode, const void* logits, int64_t row_stride, const void* e1, const void* e2,
              int32_t num_rows, int32_t k, const void* indices, int32_t force_g) {
-  if (num_rows < 0 || !k_ok(k) || row_stride < 1 || force_g < 0 || force_g > kMaxWgsPerRow)
+  if (num_rows < 0 || !k_ok(k) || row_stride < 1 || row_stride >= ((int64_t)1 << 30) ||
+      force_g < 0 || force_g > kMaxWgsPerRow)
     return TOPK_EINVAL;
   if (num_rows == 0) return TOPK_OK;
   if (!logits || !indices || !e1 || (mode == 1 && !e2)) return TOPK_EINVAL;
@@ -215,10 +216,12 @@ int device_info(DevInfo** out, int* dev_out) {
 
 int run(int mode, const float* logits, int64_t row_stride, const int32_t* e1, const int32_t* e2,
         int32_t num_rows, int32_t k, int32_t* indices, int64_t max_row_len, void* workspace,
-        size_t workspace_bytes, hipStream_t stream, const topk_options* opts) {
+        size_t workspace_bytes, hipStream_t stream, const topk_options* opts,
+        const VarlenForm* vf = nullptr) {
   const int32_t force_g = opts ? opts->force_wgs_per_row : 0;
   int rc = validate(mode, logits, row_stride, e1, e2, num_rows, k, indices, force_g);
   if (rc != TOPK_OK) return rc;
+  if (vf && num_rows > 0 && (vf->next_n < 1 || vf->compress_ratio < 1)) return TOPK_EINVAL;
   if (opts && opts->row_stats && !aligned(opts->row_stats, 4)) return TOPK_ELAYOUT;
   const uint32_t flags = opts ? opts->flags : 0u;
   float* values = opts ? opts->values : nullptr;
@@ -278,9 +281,10 @@ int run(int mode, const float* logits, int64_t row_stride, const int32_t* e1, co
   memset(&prm, 0, sizeof(prm));
   prm.logits = logits;
   prm.row_stride = row_stride;
-  prm.n_valid = (mode == 0) ? e1 : nullptr;
+  prm.n_valid = (mode == 0 && !vf) ? e1 : nullptr;
   prm.row_starts = (mode == 1) ? e1 : nullptr;
   prm.row_ends = (mode == 1) ? e2 : nullptr;
+  if (vf) prm.varlen = VarlenForm{e1, vf->next_n, vf->compress_ratio};
   prm.wgs_per_row = pl.G;
   prm.cap = pl.cap;
   prm.force_rescue = (opts && opts->force_rescue) ? 1 : 0;
@@ -315,6 +319,7 @@ int run(int mode, const float* logits, int64_t row_stride, const int32_t* e1, co
     ep.n_valid = prm.n_valid;
     ep.row_starts = prm.row_starts;
     ep.row_ends = prm.row_ends;
+    ep.varlen = prm.varlen;
     ep.sorted = (flags & TOPK_SORTED) ? 1 : 0;
     ep.indices = indices;
     ep.values = values;
@@ -370,6 +375,28 @@ int topk_prefill_v(const float* logits, int64_t row_stride, const int32_t* row_s
   o.flags = flags;
   return run(1, logits, row_stride, row_starts, row_ends, num_rows, k, indices, max_row_len,
              workspace, workspace_bytes, stream, &o);
+}
+
+int topk_decode_varlen(const float* logits, int64_t row_stride, const int32_t* kv_lens,
+                       int32_t num_rows, int32_t next_n, int32_t compress_ratio, int32_t k,
+                       int32_t* indices, float* values, uint32_t flags, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  topk_options o;
+  memset(&o, 0, sizeof(o));
+  o.values = values;
+  o.flags = flags;
+  const VarlenForm vf{kv_lens, next_n, compress_ratio};
+  return run(0, logits, row_stride, kv_lens, nullptr, num_rows, k, indices, 0, workspace,
+             workspace_bytes, stream, &o, &vf);
+}
+
+int topk_decode_varlen_ex(const float* logits, int64_t row_stride, const int32_t* kv_lens,
+                          int32_t num_rows, int32_t next_n, int32_t compress_ratio, int32_t k,
+                          int32_t* indices, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream, const topk_options* opts) {
+  const VarlenForm vf{kv_lens, next_n, compress_ratio};
+  return run(0, logits, row_stride, kv_lens, nullptr, num_rows, k, indices, 0, workspace,
+             workspace_bytes, stream, opts, &vf);
 }
 
 int topk_decode_ex(const float* logits, int64_t row_stride, const int32_t* n_valid,

@@ -73,7 +73,8 @@ extern "C" {
 enum {
   TOPK_OK = 0,
   TOPK_EINVAL = 1,     /* null pointer with num_rows > 0, num_rows < 0, k not in
-                          {512,1024,2048}, row_stride < 1, bad option value */
+                          {512,1024,2048}, row_stride < 1 or >= 2^30, bad option
+                          value, a row longer than the largest launch plan */
   TOPK_ELAYOUT = 2,    /* logits not 16-byte aligned, row_stride % 4 != 0,
                           indices / extents not 4-byte aligned */
   TOPK_EWORKSPACE = 3, /* caller workspace smaller than topk_workspace_bytes */
@@ -126,6 +127,20 @@ int topk_prefill_v(const float* logits, int64_t row_stride, const int32_t* row_s
                    float* values, uint32_t flags, int64_t max_row_len, void* workspace,
                    size_t workspace_bytes, hipStream_t stream);
 
+/* Varlen / MTP decode form (PR 18122, run_varlen commit: the production
+ * decode contract): kv_lens is a device int32 array with one TOTAL cache length
+ * per request, in uncompressed token space; row r belongs to request
+ * r / next_n and selects from logits[r, 0:n) with
+ *     n = (kv_lens[r / next_n] - next_n + r % next_n + 1) / compress_ratio
+ * (integer division), no window when kv_lens[r / next_n] < next_n, and n
+ * clamped to row_stride.  kv_lens needs ceil(num_rows / next_n) entries.
+ * next_n >= 1 (MTP rows per request) and compress_ratio >= 1 (1 and 4 in the
+ * pages' models), else TOPK_EINVAL.  values / flags as in topk_decode_v. */
+int topk_decode_varlen(const float* logits, int64_t row_stride, const int32_t* kv_lens,
+                       int32_t num_rows, int32_t next_n, int32_t compress_ratio, int32_t k,
+                       int32_t* indices, float* values, uint32_t flags, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
+
 /* Bytes of workspace a call with num_rows rows of stride `max_row_len` needs
  * (pass the row_stride of the call; 0 when the plan uses one workgroup per
  * row and needs none).  The value does not depend on the device.  Returns 0
@@ -174,6 +189,11 @@ int topk_prefill_ex(const float* logits, int64_t row_stride, const int32_t* row_
                     const int32_t* row_ends, int32_t num_rows, int32_t k, int32_t* indices,
                     int64_t max_row_len, void* workspace, size_t workspace_bytes,
                     hipStream_t stream, const topk_options* opts);
+
+int topk_decode_varlen_ex(const float* logits, int64_t row_stride, const int32_t* kv_lens,
+                          int32_t num_rows, int32_t next_n, int32_t compress_ratio, int32_t k,
+                          int32_t* indices, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream, const topk_options* opts);
 
 /* Host-only planning and validation, callable without a GPU.  Fills
  * out[0..6] = {workgroups per row, float4 groups per thread, rows per launch,

@@ -109,6 +109,34 @@ def topk_window(w: np.ndarray, k: int) -> np.ndarray:
     return out
 
 
+def varlen_n_valid(kv_lens, num_rows: int, next_n: int, compress_ratio: int,
+                   row_stride: int) -> np.ndarray:
+    """Valid length of each row of the varlen / MTP decode form.
+
+    "Block-skip fast path ..." (PR 18122), run_varlen commit: kv_lens holds one
+    total cache length per request (uncompressed token space); row r belongs
+    to request r // next_n and sees
+        n = (kv_len - next_n + r % next_n + 1) // compress_ratio
+    positions; a request with kv_len < next_n has empty rows (its "next_n"
+    query tokens are not all in the cache yet).  The boundary then clamps n
+    to the row stride.  Plain Python integers, one row at a time.
+    """
+    out = np.zeros(num_rows, dtype=np.int64)
+    for r in range(num_rows):
+        kv = int(kv_lens[r // next_n])
+        n = 0 if kv < next_n else (kv - next_n + r % next_n + 1) // compress_ratio
+        out[r] = min(max(n, 0), row_stride)
+    return out
+
+
+def topk_varlen(logits: np.ndarray, kv_lens, next_n: int, compress_ratio: int, k: int):
+    """Exact top-k per row of a varlen / MTP decode batch: the decode form on
+    the windows ``varlen_n_valid`` gives."""
+    x = np.asarray(logits)
+    nv = varlen_n_valid(kv_lens, x.shape[0], next_n, compress_ratio, x.shape[1])
+    return topk_decode(x, nv.astype(np.int32), k)
+
+
 def topk_workload(w) -> np.ndarray:
     """Oracle output for a ``workloads.Workload``."""
     if w.mode == "decode":

@@ -141,3 +141,24 @@ def test_plan_forced_tiers():
         ert.plan_query(8, 4096, 512, force_wgs_per_row=65)
     with pytest.raises(ert.TopKError):
         ert.plan_query(1, 64 * 17 * 256 * 4 + 64, 512)        # longer than the largest plan
+
+
+def test_output_options_and_varlen_validation():
+    lib = ert.load_library()
+    # bad next_n / compression ratio, unknown flag bits, misaligned values: all
+    # rejected on the host before any device work
+    assert lib.topk_decode_varlen(P16, 4096, P16, 4, 0, 1, 512, P16, None, 0, None, 0,
+                                  None) == ert.TOPK_EINVAL
+    assert lib.topk_decode_varlen(P16, 4096, P16, 4, 2, 0, 512, P16, None, 0, None, 0,
+                                  None) == ert.TOPK_EINVAL
+    assert lib.topk_decode_varlen(P16, 4096, P16, 4, 2, 4, 513, P16, None, 0, None, 0,
+                                  None) == ert.TOPK_EINVAL
+    assert lib.topk_decode_v(P16, 4096, P16, 4, 512, P16, None, 4, None, 0, None) == ert.TOPK_EINVAL
+    assert lib.topk_decode_v(P16, 4096, P16, 4, 512, P16, P16 + 2, 0, None, 0,
+                             None) == ert.TOPK_ELAYOUT
+    assert lib.topk_prefill_v(P16, 4096, P16, P16, 4, 512, P16, None, 8, 0, None, 0,
+                              None) == ert.TOPK_EINVAL
+    # empty batches are a no-op for every form
+    assert lib.topk_decode_varlen(None, 4096, None, 0, 2, 4, 512, None, None, 0, None, 0,
+                                  None) == 0
+    assert _validate(stride=1 << 30) == ert.TOPK_EINVAL

@@ -306,3 +306,45 @@ def test_workload_shapes_and_bytes():
     hot = w4.logits[0, :114963] > 120
     assert 1100 < int(hot.sum()) <= 1150
     assert int(hot[: int(0.8 * 114963)].sum()) == 0
+
+
+# ---- varlen / MTP decode form ---------------------------------------------------
+
+@pytest.mark.parametrize("case", load_golden("varlen_windows.txt"), ids=lambda c: c["case"])
+def test_varlen_windows_golden(case):
+    kv = [int(t) for t in case["kv_lens"].split()]
+    got = oracle.varlen_n_valid(kv, int(case["rows"]), int(case["next_n"]), int(case["cr"]),
+                                int(case["stride"]))
+    assert got.tolist() == [int(t) for t in case["expect"].split()]
+
+
+def test_varlen_window_properties():
+    rng = np.random.default_rng(5)
+    for next_n in (1, 2, 3, 4):
+        for cr in (1, 4):
+            kv = rng.integers(0, 5000, size=17)
+            rows = 17 * next_n
+            n = oracle.varlen_n_valid(kv, rows, next_n, cr, 1 << 20)
+            for q in range(17):
+                seg = n[q * next_n:(q + 1) * next_n]
+                if kv[q] < next_n:
+                    assert np.all(seg == 0)
+                    continue
+                # the last MTP row sees the whole (compressed) cache
+                assert seg[-1] == kv[q] // cr
+                # later MTP rows never see less, and with cr = 1 one more each
+                assert np.all(np.diff(seg) >= 0)
+                if cr == 1:
+                    assert np.all(np.diff(seg) == 1)
+            if next_n == 1 and cr == 1:
+                assert np.array_equal(n, kv)  # the plain decode form
+
+
+def test_varlen_oracle_is_decode_on_its_windows():
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((8, 3000)).astype(np.float32)
+    kv = np.array([2999, 1200, 1, 2400], dtype=np.int32)
+    got = oracle.topk_varlen(x, kv, 2, 1, 512)
+    nv = np.array([2998, 2999, 1199, 1200, 0, 0, 2399, 2400], dtype=np.int32)
+    assert np.array_equal(got, oracle.topk_decode(x, nv, 512))
+    assert got[4].tolist() == [-1] * 512
