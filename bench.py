@@ -36,7 +36,8 @@ sys.path.insert(0, ROOT)
 METRIC = "top-K rows/s + achieved HBM GB/s vs peak; p50/p99 µs/row, K=512..2048"
 PEAK_HBM_GBS = 8000.0  # MI355X published HBM3E bandwidth
 ROTATE_BYTES = 1 << 30
-KERNEL_SOURCES = ("exact_row_top_amd/csrc/gvr_kernels.hip", "exact_row_top_amd/csrc/gvr_common.h")
+KERNEL_SOURCES = ("exact_row_top_amd/csrc/gvr_kernels.hip", "exact_row_top_amd/csrc/gvr_common.h",
+                  "exact_row_top_amd/csrc/row_window.h")
 
 
 def log(*a):

@@ -288,6 +288,18 @@ struct Cross {
   uint32_t total;
 };
 
+// The crossing that find_crossing left in LDS, held in scalar registers (every
+// lane reads the same words; readfirstlane keeps them out of the VGPR budget
+// the resident row needs).
+__device__ __forceinline__ Cross read_cross(const Cross* c) {
+  Cross r;
+  r.b = __builtin_amdgcn_readfirstlane(c->b);
+  r.above = __builtin_amdgcn_readfirstlane(c->above);
+  r.m = __builtin_amdgcn_readfirstlane(c->m);
+  r.total = __builtin_amdgcn_readfirstlane(c->total);
+  return r;
+}
+
 // Find the highest bin b with sum_{b' >= b} h[b'] >= target over NBINS bins,
 // where load(b) returns h[b].  Thread t owns PER consecutive bins from the
 // top.  Result in *out (LDS), visible to all threads on return.
@@ -483,7 +495,7 @@ __device__ __forceinline__ RSel radix_select(Iter&& iter, uint32_t need, uint32_
     } else {
       find_crossing<256, BLOCK>([&](int d) { return dh[d]; }, rem, cross, scan);
     }
-    const Cross c = *cross;
+    const Cross c = read_cross(cross);
     prefix |= (uint32_t)c.b << shift;
     rem -= c.above;
     cnt = c.m;
@@ -559,15 +571,19 @@ struct alignas(16) Smem {
   uint32_t ctr[4];
 };
 
-// Occupancy the one-workgroup variants with up to 9 groups per thread and up
-// to 512 threads are compiled for (K <= 1024 for 512 threads): eight waves
-// per SIMD (64 VGPRs), so that four 512-thread workgroups share a compute
-// unit.  The others keep the compiler's choice (at 64 VGPRs they would
-// spill).
+// Occupancy targets of the one-workgroup variants (waves per SIMD; the VGPR
+// budget is 512 / waves, in granules of 8):
+//  * up to 9 groups per thread and up to 512 threads: 8 (64 VGPRs), so that
+//    four 512-thread workgroups share a compute unit;
+//  * 256 threads and 17 groups: 5 (96 VGPRs; one more granule would drop a
+//    wave per SIMD, about 10 % of a full-chip pass).
+// The split variants and the 1024-thread one keep the compiler's choice.
 template <int K, int QPT, int BLOCK, bool SPLIT>
 struct WavesPerEu {
-  static constexpr int value =
-      (SPLIT || QPT > 9 || BLOCK > 512 || (BLOCK == 512 && K > 1024)) ? 1 : 8;
+  static constexpr int value = SPLIT                          ? 1
+                               : (BLOCK <= 512 && QPT <= 9)   ? 8
+                               : (BLOCK == 256 && QPT == 17)  ? 5
+                                                              : 1;
 };
 
 template <int K, int QPT, int BLOCK, bool SPLIT>
@@ -818,7 +834,7 @@ __global__ void __launch_bounds__(BLOCK)
       __syncthreads();
       find_crossing<kBins, BLOCK>([&](int b) { return sm.u.hist[b]; }, (uint32_t)K, &sm.cross,
                                   sm.scan);
-      cr = sm.cross;
+      cr = read_cross(&sm.cross);
       path = (cr.b >= 0 && cr.m <= (uint32_t)kSingleCap) ? 1 : 3;
     }
     if (path == 1) {
@@ -925,7 +941,7 @@ __global__ void __launch_bounds__(BLOCK)
       const float rl = lam + 4.0f * sqrtf(lam) + 8.0f;
       const uint32_t rlow = rl >= (float)K ? (uint32_t)K : (uint32_t)rl;
       find_crossing<kBins, BLOCK>([&](int b) { return sm.u.hist[b]; }, rlow, &sm.cross, sm.scan);
-      const Cross sc0 = sm.cross;
+      const Cross sc0 = read_cross(&sm.cross);
       blo = sc0.b > 0 ? sc0.b : 0;
       // A sample bin at or above the floor holding 8 or more samples marks a
       // row with heavy ties there: its histogram pass aggregates per wave.
@@ -1016,7 +1032,7 @@ __global__ void __launch_bounds__(BLOCK)
       // ---- crossing bin (a5), the same in every workgroup of the row -----
       find_crossing<kBins, BLOCK>([&](int b) { return sm.u.hist[b]; }, (uint32_t)K, &sm.cross,
                                   sm.scan);
-      cr = sm.cross;
+      cr = read_cross(&sm.cross);
       // Merged counts below K (the sample's floor lay above the K-th value)
       // or a crowded crossing bin: the row's workgroups take the rescue
       // together.
