@@ -108,7 +108,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=2, help="1..5 (2 is the headline batch)")
+    ap.add_argument("--workload", type=int, default=2,
+                    help="1..5 (2 is the headline batch); 6 = workload 2's shape as a decode "
+                         "step with the previous step's top-K as hints")
+    ap.add_argument("--no-hints", action="store_true",
+                    help="workload 6 without its hints (the same rows, sample-only guess)")
     ap.add_argument("--bs", type=int, default=1, help="batch size for workload 4")
     ap.add_argument("--warm", action="store_true", help="no rotation: inputs stay cache-resident")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline leg")
@@ -134,10 +138,20 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     ert.load_library()
-    kw = {"bs": args.bs} if args.workload == 4 else {}
-    w = workloads.config(args.workload, **kw)
+    hints = None
+    if args.workload == 6:
+        w, hints = workloads.decode_step()
+        if args.no_hints:
+            hints = None
+            w.name = w.name.replace("_hinted", "_unhinted")
+    else:
+        kw = {"bs": args.bs} if args.workload == 4 else {}
+        w = workloads.config(args.workload, **kw)
     rows, k = w.num_rows, w.k
     alg_bytes = w.algorithmic_bytes()
+    if hints is not None:
+        # a long row's hint row is read once (short rows read none)
+        alg_bytes += 4 * k * int((w.valid_lengths() > k).sum())
     log(f"[bench] workload {w.name}: {rows} rows, stride {w.row_stride}, k={k}, "
         f"algorithmic bytes/launch {alg_bytes}")
 
@@ -145,6 +159,9 @@ def main():
     if w.mode == "decode":
         ext = (torch.from_numpy(w.n_valid).cuda(),)
         fn = ert.topk_decode
+        if hints is not None:
+            dev_h = torch.from_numpy(hints).cuda()
+            fn = lambda *a, **kw: ert.topk_decode(*a, pre_idx=dev_h, **kw)  # noqa: E731
     else:
         ext = (torch.from_numpy(w.row_starts).cuda(), torch.from_numpy(w.row_ends).cuda())
         fn = ert.topk_prefill

@@ -19,7 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libexact_row_top.so")
 
 TOPK_OK, TOPK_EINVAL, TOPK_ELAYOUT, TOPK_EWORKSPACE, TOPK_EDEVICE, TOPK_ELAUNCH = range(6)
-STATS_WORDS = 8
+STATS_WORDS = 9
 VALID_K = (512, 1024, 2048)
 
 _lib = None
@@ -36,7 +36,9 @@ class _Options(ctypes.Structure):
                 ("force_rescue", ctypes.c_int32),
                 ("row_stats", ctypes.c_void_p),
                 ("values", ctypes.c_void_p),
-                ("flags", ctypes.c_uint32)]
+                ("flags", ctypes.c_uint32),
+                ("pre_idx", ctypes.c_void_p),
+                ("pre_idx_stride", ctypes.c_int64)]
 
 
 TOPK_SORTED = 1
@@ -63,6 +65,12 @@ def load_library():
     lib.topk_decode_varlen.argtypes = [P, I64, P, I32, I32, I32, I32, P, P, ctypes.c_uint32, P,
                                        SZ, P]
     lib.topk_decode_varlen.restype = ctypes.c_int
+    lib.topk_decode_hinted.argtypes = [P, I64, P, P, I64, I32, I32, P, P, ctypes.c_uint32, P,
+                                       SZ, P]
+    lib.topk_decode_hinted.restype = ctypes.c_int
+    lib.topk_decode_varlen_hinted.argtypes = [P, I64, P, P, I64, I32, I32, I32, I32, P, P,
+                                              ctypes.c_uint32, P, SZ, P]
+    lib.topk_decode_varlen_hinted.restype = ctypes.c_int
     lib.topk_decode_varlen_ex.argtypes = [P, I64, P, I32, I32, I32, I32, P, P, SZ, P,
                                           ctypes.POINTER(_Options)]
     lib.topk_decode_varlen_ex.restype = ctypes.c_int
@@ -186,7 +194,7 @@ def _out(indices, rows, k, device):
     return indices
 
 
-def _opts(force_wgs_per_row, force_rescue, row_stats, rows, values=None, flags=0):
+def _opts(force_wgs_per_row, force_rescue, row_stats, rows, values=None, flags=0, hints=None):
     import torch
     if not (force_wgs_per_row or force_rescue or row_stats is not None):
         return None
@@ -196,7 +204,8 @@ def _opts(force_wgs_per_row, force_rescue, row_stats, rows, values=None, flags=0
             raise ValueError(f"row_stats must be a contiguous int32 [{rows}, {STATS_WORDS}] tensor")
     o = _Options(int(force_wgs_per_row), int(bool(force_rescue)),
                  row_stats.data_ptr() if row_stats is not None else None,
-                 values.data_ptr() if values is not None else None, int(flags))
+                 values.data_ptr() if values is not None else None, int(flags),
+                 hints[0] if hints else None, hints[1] if hints else 0)
     return ctypes.pointer(o)
 
 
@@ -213,6 +222,21 @@ def _values(values, return_values, rows, k, device):
     return values
 
 
+def _hints(pre_idx, requests, k, device):
+    """(pointer, stride) of a hint tensor: int32 [>= requests, >= k], unit
+    inner stride; or None."""
+    import torch
+    if pre_idx is None:
+        return None
+    _require(pre_idx, "pre_idx", torch.int32, 2)
+    if pre_idx.device != device:
+        raise ValueError(f"pre_idx must be on {device}")
+    if pre_idx.shape[0] < requests or pre_idx.shape[1] < k or pre_idx.stride(1) != 1:
+        raise ValueError(f"pre_idx must be int32 [>= {requests}, >= {k}] with unit inner stride")
+    stride = pre_idx.stride(0) if pre_idx.shape[0] > 1 else pre_idx.shape[1]
+    return pre_idx.data_ptr(), int(stride)
+
+
 def _flags(sorted_, deterministic):
     return (TOPK_SORTED if sorted_ else 0) | (TOPK_DETERMINISTIC if deterministic else 0)
 
@@ -225,14 +249,16 @@ def _ws(workspace):
 
 def topk_decode(logits, n_valid, k: int, indices=None, *, workspace=None, stream=None,
                 values=None, return_values: bool = False, sorted: bool = False,
-                deterministic: bool = False, force_wgs_per_row: int = 0,
+                deterministic: bool = False, pre_idx=None, force_wgs_per_row: int = 0,
                 force_rescue: bool = False, row_stats=None):
     """Exact top-k of logits[r, :n_valid[r]] per row (local indices, -1 pad).
 
     values / return_values: also the selected scores (-FLT_MAX pad); sorted:
     long rows ordered by value descending, then index ascending;
-    deterministic: the k-th value's ties resolved by smallest index.  Returns
-    the indices, or (indices, values) when values are asked for."""
+    deterministic: the k-th value's ties resolved by smallest index; pre_idx:
+    optional int32 [rows, >= k] hints (the previous step's top-k positions),
+    which steer the guess only.  Returns the indices, or (indices, values)
+    when values are asked for."""
     import torch
     lib = load_library()
     rows, row_stride = _logits_layout(logits)
@@ -242,12 +268,18 @@ def topk_decode(logits, n_valid, k: int, indices=None, *, workspace=None, stream
     out = _out(indices, rows, k, logits.device)
     vals = _values(values, return_values, rows, k, logits.device)
     flags = _flags(sorted, deterministic)
+    hints = _hints(pre_idx, rows, k, logits.device)
     wp, wb = _ws(workspace)
-    opts = _opts(force_wgs_per_row, force_rescue, row_stats, rows, vals, flags)
+    opts = _opts(force_wgs_per_row, force_rescue, row_stats, rows, vals, flags, hints)
     s = _stream_ptr(stream, logits.device)
     if opts is not None:
         rc = lib.topk_decode_ex(logits.data_ptr(), row_stride, n_valid.data_ptr(), rows, k,
                                 out.data_ptr(), wp, wb, s, opts)
+    elif hints is not None:
+        rc = lib.topk_decode_hinted(logits.data_ptr(), row_stride, n_valid.data_ptr(), hints[0],
+                                    hints[1], rows, k, out.data_ptr(),
+                                    vals.data_ptr() if vals is not None else None, flags, wp, wb,
+                                    s)
     elif vals is not None or flags:
         rc = lib.topk_decode_v(logits.data_ptr(), row_stride, n_valid.data_ptr(), rows, k,
                                out.data_ptr(), vals.data_ptr() if vals is not None else None,
@@ -299,13 +331,14 @@ def topk_prefill(logits, row_starts, row_ends, k: int, indices=None, *, max_row_
 def topk_decode_varlen(logits, kv_lens, k: int, next_n: int = 1, compress_ratio: int = 1,
                        indices=None, *, workspace=None, stream=None, values=None,
                        return_values: bool = False, sorted: bool = False,
-                       deterministic: bool = False, force_wgs_per_row: int = 0,
+                       deterministic: bool = False, pre_idx=None, force_wgs_per_row: int = 0,
                        force_rescue: bool = False, row_stats=None):
     """Exact top-k of the varlen / MTP decode form: row r selects from
     logits[r, :n] with n = (kv_lens[r // next_n] - next_n + r % next_n + 1) //
     compress_ratio (no window when kv_lens[r // next_n] < next_n), computed on
-    the device from the per-request kv_lens.  Output options as for
-    topk_decode."""
+    the device from the per-request kv_lens.  pre_idx: optional int32
+    [requests, >= k] hints, one row per request shared by its next_n rows.
+    Output options as for topk_decode."""
     import torch
     lib = load_library()
     rows, row_stride = _logits_layout(logits)
@@ -316,13 +349,20 @@ def topk_decode_varlen(logits, kv_lens, k: int, next_n: int = 1, compress_ratio:
     out = _out(indices, rows, k, logits.device)
     vals = _values(values, return_values, rows, k, logits.device)
     flags = _flags(sorted, deterministic)
+    hints = _hints(pre_idx, need, k, logits.device)
     wp, wb = _ws(workspace)
-    opts = _opts(force_wgs_per_row, force_rescue, row_stats, rows, vals, flags)
+    opts = _opts(force_wgs_per_row, force_rescue, row_stats, rows, vals, flags, hints)
     s = _stream_ptr(stream, logits.device)
     if opts is not None:
         rc = lib.topk_decode_varlen_ex(logits.data_ptr(), row_stride, kv_lens.data_ptr(), rows,
                                        int(next_n), int(compress_ratio), k, out.data_ptr(), wp, wb,
                                        s, opts)
+    elif hints is not None:
+        rc = lib.topk_decode_varlen_hinted(logits.data_ptr(), row_stride, kv_lens.data_ptr(),
+                                           hints[0], hints[1], rows, int(next_n),
+                                           int(compress_ratio), k, out.data_ptr(),
+                                           vals.data_ptr() if vals is not None else None, flags,
+                                           wp, wb, s)
     else:
         rc = lib.topk_decode_varlen(logits.data_ptr(), row_stride, kv_lens.data_ptr(), rows,
                                     int(next_n), int(compress_ratio), k, out.data_ptr(),

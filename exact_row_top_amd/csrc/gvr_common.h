@@ -38,7 +38,7 @@ constexpr int kSplitQpt[] = {4, 8, 17};
 
 constexpr int kMaxWgsPerRow = 64;
 constexpr int kMaxSlots = 256;  // split rows per launch (workspace slots)
-constexpr int kStatsWords = 8;
+constexpr int kStatsWords = 9;
 
 // Workspace layout (bytes):
 //   [0, 256)                             error flags (word 0)
@@ -112,6 +112,9 @@ struct GvrParams {
   int32_t cap;        // candidate cap of this plan
   int32_t force_rescue;
   int32_t deterministic;  // resolve the K-th value's tie class by smallest index
+  const int32_t* hints;   // optional previous-step top-K positions (guess only)
+  int64_t hint_stride;    // int32 entries between consecutive hint rows
+  int32_t hint_div;       // row r reads hint row r / hint_div
   int32_t* indices;
   int32_t* row_stats;  // optional
   unsigned char* ws;   // workspace base (split tier), or nullptr

@@ -565,6 +565,8 @@ struct alignas(16) Smem {
   uint32_t scan[BLOCK / 64];
   float rmin[BLOCK / 64];
   float rmax[BLOCK / 64];
+  float hmin[BLOCK / 64];
+  float hmax[BLOCK / 64];
   Cross cross;
   float thr[2];
   uint32_t bc[4];
@@ -573,15 +575,16 @@ struct alignas(16) Smem {
 
 // Occupancy targets of the one-workgroup variants (waves per SIMD; the VGPR
 // budget is 512 / waves, in granules of 8):
-//  * up to 9 groups per thread and up to 512 threads: 8 (64 VGPRs), so that
-//    four 512-thread workgroups share a compute unit;
+//  * up to 9 groups per thread and 256 threads, or 512 threads for K <= 1024:
+//    8 (64 VGPRs), so that four 512-thread workgroups share a compute unit
+//    (512 threads at K = 2048 would spill there);
 //  * 256 threads and 17 groups: 5 (96 VGPRs; one more granule would drop a
 //    wave per SIMD, about 10 % of a full-chip pass).
 // The split variants and the 1024-thread one keep the compiler's choice.
 template <int K, int QPT, int BLOCK, bool SPLIT>
 struct WavesPerEu {
   static constexpr int value = SPLIT                          ? 1
-                               : (BLOCK <= 512 && QPT <= 9)   ? 8
+                               : (QPT <= 9 && (BLOCK == 256 || (BLOCK == 512 && K <= 1024))) ? 8
                                : (BLOCK == 256 && QPT == 17)  ? 5
                                                               : 1;
 };
@@ -685,6 +688,44 @@ __global__ void __launch_bounds__(BLOCK)
     }
   }
 
+  // ---- hint-guided guess (a3 variant): positions ---------------------------
+  // Optional: the caller's hint positions -- the previous decode step's top-K
+  // of the same request, raw, possibly stale or degenerate.  They only steer
+  // the bracket; every later step is exact whatever they hold.  Each thread
+  // takes one hint slot (the first min(K, BLOCK) slots): one gather per
+  // thread instead of K / BLOCK keeps the dependent, line-per-lane loads
+  // cheap, and the extremes over a few hundred hint scores already sit near
+  // those of the whole hint set.  The split tier reads them up front: its
+  // positions first, so that the scores are gathered before the part's loads
+  // are issued and the bracket overlaps the part's flight as it does without
+  // hints.  A one-workgroup row reads them only when its first bracket fails
+  // (below): there a retry costs one histogram pass in LDS.
+  const int32_t* hrow = nullptr;
+  if (p.hints) {
+    // rows and hint_div are positive int32: a 32-bit unsigned divide
+    const uint32_t req = (uint32_t)row / (uint32_t)p.hint_div;
+    hrow = p.hints + (int64_t)req * p.hint_stride;
+  }
+  int32_t hpos = -1;
+  if (SPLIT && hrow && t < K) hpos = hrow[t];
+
+  // ---- hint-guided guess: scores -------------------------------------------
+  // A hint outside [0, nv) (the -1 pad of a short row, a position past the
+  // window) is skipped by an unsigned compare; a NaN leaves min / max as is.
+  if (SPLIT && hrow) {
+    float x = qnan;
+    if ((uint32_t)hpos < (uint32_t)nv) x = rowp[ks + hpos];
+    float hlo = x, hhi = x;
+    wave_minmax(hlo, hhi);
+    if (l == 0) {
+      sm.hmin[w] = hlo;
+      sm.hmax[w] = hhi;
+    }
+    // keep the part's loads behind this point: issued earlier, they would
+    // hold their registers while the gather waits (loads complete in order)
+    asm volatile("" ::: "memory");
+  }
+
   // ---- scan (a2): the part, resident in VGPRs -----------------------------
   // Thread t holds groups q0 + t + j * BLOCK, j < QPT: each load instruction
   // of a wave reads 1 KiB of consecutive scores.  Lanes outside the window or
@@ -756,6 +797,39 @@ __global__ void __launch_bounds__(BLOCK)
     gmin = fminf(gmin, sm.rmin[i]);
     gmax = fmaxf(gmax, sm.rmax[i]);
   }
+  // uniform: scalar registers, out of the resident row's VGPR budget
+  gmin = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(gmin)));
+  gmax = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(gmax)));
+  // Usable hints (finite, at least two distinct scores) raise the bracket's
+  // top to the highest hint score when it lies above the sample's maximum:
+  // peaks the sample missed then get bins of their own instead of piling up
+  // in the top bin.  The split tier also lets the lowest hint score lower its
+  // floor (below).  Degenerate hints (all one position, all invalid, all -1)
+  // change nothing.
+  // (the per-wave extremes in sm.hmin / sm.hmax, reduced over the workgroup)
+  auto hint_extremes = [&](float& hl, float& hh) {
+    hl = sm.hmin[0];
+    hh = sm.hmax[0];
+#pragma unroll
+    for (int i = 1; i < W; ++i) {
+      hl = fminf(hl, sm.hmin[i]);
+      hh = fmaxf(hh, sm.hmax[i]);
+    }
+    // every lane read the same words: keep them in scalar registers
+    hl = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(hl)));
+    hh = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(hh)));
+  };
+  bool hint_ok = false;
+  float hfloor = 0.0f;
+  if (SPLIT && hrow) {
+    float hl, hh;
+    hint_extremes(hl, hh);
+    if (__builtin_isfinite(hl) && __builtin_isfinite(hh) && hh > hl) {
+      hint_ok = true;
+      hfloor = hl;
+      gmax = fmaxf(gmax, hh);
+    }
+  }
   const float range = gmax - gmin;
   BinMap bm;
   bm.gmin = gmin;
@@ -798,6 +872,7 @@ __global__ void __launch_bounds__(BLOCK)
     }
   }
 
+  int floor_bin = -1;  // split tier: the floor bin its histogram counts from
   auto put_stats = [&](int path, int m, int above, int b) {
     if (stats && t == 0) {
       stats[0] = path;
@@ -808,6 +883,7 @@ __global__ void __launch_bounds__(BLOCK)
       stats[5] = (int)__float_as_uint(gmax);
       stats[6] = G;
       stats[7] = p.cap;
+      stats[8] = floor_bin;
     }
   };
 
@@ -819,23 +895,61 @@ __global__ void __launch_bounds__(BLOCK)
     // ==== one workgroup per row ============================================
     if (bracket_ok) {
       // ---- verify (a4, a5): LDS histogram and crossing bin ---------------
-      each([&](int j, int q, bool full) {
-        if (full) {
+      auto verify = [&]() {
+        each([&](int j, int q, bool full) {
+          if (full) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) lds_inc(hword(sm.u.hist, vbin_off(v[j][e], bm)));
-        } else {
+            for (int e = 0; e < 4; ++e) lds_inc(hword(sm.u.hist, vbin_off(v[j][e], bm)));
+          } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float x = v[j][e];
-            lds_inc(hword(sm.u.hist, (x == x) ? vbin_off(x, bm) : 4u * (uint32_t)(kBins + l)));
+            for (int e = 0; e < 4; ++e) {
+              const float x = v[j][e];
+              lds_inc(hword(sm.u.hist, (x == x) ? vbin_off(x, bm) : 4u * (uint32_t)(kBins + l)));
+            }
+          }
+        });
+        __syncthreads();
+        find_crossing<kBins, BLOCK>([&](int b) { return sm.u.hist[b]; }, (uint32_t)K, &sm.cross,
+                                    sm.scan);
+        cr = read_cross(&sm.cross);
+        path = (cr.b >= 0 && cr.m <= (uint32_t)kSingleCap) ? 1 : 3;
+      };
+      verify();
+      if (path == 3 && hrow) {
+        // Hint-guided retry: the crossing bin is over the cap.  When the
+        // hints reach above the sample's maximum (peaks the sample missed,
+        // piled into the top bin), raise the bracket's top to them and
+        // count again; otherwise the rescue below finishes the row.
+        float x = qnan;
+        if (t < K) {
+          const int32_t hp = hrow[t];
+          if ((uint32_t)hp < (uint32_t)nv) x = rowp[ks + hp];
+        }
+        float hlo = x, hhi = x;
+        wave_minmax(hlo, hhi);
+        if (l == 0) {
+          sm.hmin[w] = hlo;
+          sm.hmax[w] = hhi;
+        }
+        __syncthreads();
+        float hl, hh;
+        hint_extremes(hl, hh);
+        if (__builtin_isfinite(hl) && __builtin_isfinite(hh) && hh > hl && hh > gmax) {
+          const float sc = (float)kBins / (hh - gmin);
+          const float c0 = -gmin * sc;
+          if (__builtin_isfinite(hh - gmin) && __builtin_isfinite(4.0f * sc) &&
+              __builtin_isfinite(4.0f * c0) && sc > 0.0f) {
+            gmax = hh;
+            bm.sc = sc;
+            bm.c0 = c0;
+            bm.sc4 = 4.0f * sc;
+            bm.c04 = 4.0f * c0;
+            for (int i = t; i < kBins + 64; i += BLOCK) sm.u.hist[i] = 0u;
+            __syncthreads();
+            verify();
           }
         }
-      });
-      __syncthreads();
-      find_crossing<kBins, BLOCK>([&](int b) { return sm.u.hist[b]; }, (uint32_t)K, &sm.cross,
-                                  sm.scan);
-      cr = read_cross(&sm.cross);
-      path = (cr.b >= 0 && cr.m <= (uint32_t)kSingleCap) ? 1 : 3;
+      }
     }
     if (path == 1) {
       // ---- compaction (a6) ------------------------------------------------
@@ -943,6 +1057,27 @@ __global__ void __launch_bounds__(BLOCK)
       find_crossing<kBins, BLOCK>([&](int b) { return sm.u.hist[b]; }, rlow, &sm.cross, sm.scan);
       const Cross sc0 = read_cross(&sm.cross);
       blo = sc0.b > 0 ? sc0.b : 0;
+      if (hint_ok) {
+        // Hint-guided floor: the previous step's top-K mostly stays above
+        // this step's K-th value, so a sample floor above the lowest hint
+        // score is suspect (the sample may have met a dense cluster the rest
+        // of the row does not share).  Lower the floor to the hint's bin,
+        // unless the hint sits far below where the sample puts the K-th
+        // value (stale hints at the row's bottom would only add work):
+        // the sample's count must not pass lam + 8 sqrt(lam) + 16 above it.
+        const int bh = vbin(hfloor, bm);
+        if (bh < blo) {
+          const float ru = lam + 8.0f * sqrtf(lam) + 16.0f;
+          int bup = -1;
+          if (ru < (float)K) {
+            find_crossing<kBins, BLOCK>([&](int b) { return sm.u.hist[b]; }, (uint32_t)ru,
+                                        &sm.cross, sm.scan);
+            bup = read_cross(&sm.cross).b;
+          }
+          if (bh >= bup) blo = bh;
+        }
+      }
+      floor_bin = blo;
       // A sample bin at or above the floor holding 8 or more samples marks a
       // row with heavy ties there: its histogram pass aggregates per wave.
       for (int i = t; i < kBins + 64; i += BLOCK) {

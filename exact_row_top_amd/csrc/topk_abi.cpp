@@ -227,6 +227,12 @@ int run(int mode, const float* logits, int64_t row_stride, const int32_t* e1, co
   float* values = opts ? opts->values : nullptr;
   if (flags & ~(uint32_t)(TOPK_SORTED | TOPK_DETERMINISTIC)) return TOPK_EINVAL;
   if (values && !aligned(values, 4)) return TOPK_ELAYOUT;
+  const int32_t* hints = opts ? opts->pre_idx : nullptr;
+  if (hints) {
+    if (mode != 0) return TOPK_EINVAL;  // the prefill form takes no hints
+    if (opts->pre_idx_stride < k) return TOPK_EINVAL;
+    if (!aligned(hints, 4)) return TOPK_ELAYOUT;
+  }
   if (num_rows == 0) return TOPK_OK;
   // Plans are sized for the full row stride, so any window inside it fits the
   // resident capacity; the prefill length hint is accepted but not needed.
@@ -289,6 +295,9 @@ int run(int mode, const float* logits, int64_t row_stride, const int32_t* e1, co
   prm.cap = pl.cap;
   prm.force_rescue = (opts && opts->force_rescue) ? 1 : 0;
   prm.deterministic = (flags & TOPK_DETERMINISTIC) ? 1 : 0;
+  prm.hints = hints;
+  prm.hint_stride = hints ? opts->pre_idx_stride : 0;
+  prm.hint_div = vf ? vf->next_n : 1;  // hints are per request
   prm.indices = indices;
   prm.row_stats = opts ? opts->row_stats : nullptr;
   prm.ws = ws;
@@ -385,6 +394,36 @@ int topk_decode_varlen(const float* logits, int64_t row_stride, const int32_t* k
   memset(&o, 0, sizeof(o));
   o.values = values;
   o.flags = flags;
+  const VarlenForm vf{kv_lens, next_n, compress_ratio};
+  return run(0, logits, row_stride, kv_lens, nullptr, num_rows, k, indices, 0, workspace,
+             workspace_bytes, stream, &o, &vf);
+}
+
+int topk_decode_hinted(const float* logits, int64_t row_stride, const int32_t* n_valid,
+                       const int32_t* pre_idx, int64_t pre_idx_stride, int32_t num_rows, int32_t k,
+                       int32_t* indices, float* values, uint32_t flags, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  topk_options o;
+  memset(&o, 0, sizeof(o));
+  o.values = values;
+  o.flags = flags;
+  o.pre_idx = pre_idx;
+  o.pre_idx_stride = pre_idx_stride;
+  return run(0, logits, row_stride, n_valid, nullptr, num_rows, k, indices, 0, workspace,
+             workspace_bytes, stream, &o);
+}
+
+int topk_decode_varlen_hinted(const float* logits, int64_t row_stride, const int32_t* kv_lens,
+                              const int32_t* pre_idx, int64_t pre_idx_stride, int32_t num_rows,
+                              int32_t next_n, int32_t compress_ratio, int32_t k, int32_t* indices,
+                              float* values, uint32_t flags, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  topk_options o;
+  memset(&o, 0, sizeof(o));
+  o.values = values;
+  o.flags = flags;
+  o.pre_idx = pre_idx;
+  o.pre_idx_stride = pre_idx_stride;
   const VarlenForm vf{kv_lens, next_n, compress_ratio};
   return run(0, logits, row_stride, kv_lens, nullptr, num_rows, k, indices, 0, workspace,
              workspace_bytes, stream, &o, &vf);

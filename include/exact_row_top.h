@@ -141,6 +141,34 @@ int topk_decode_varlen(const float* logits, int64_t row_stride, const int32_t* k
                        int32_t* indices, float* values, uint32_t flags, void* workspace,
                        size_t workspace_bytes, hipStream_t stream);
 
+/* ---- Hint-guided guess ----------------------------------------------------
+ * Decode forms that also take the previous decode step's top-K positions as
+ * hints (PR 18122 run_varlen commit: request-level raw pre_idx shared by a
+ * request's next_n rows; "hint-robustness" commit and PR 20998 "What
+ * changes": hints only steer the guess, exactness never depends on them).
+ *  pre_idx: device int32, one row of at least k entries per request (per row
+ *      in the plain decode form), pre_idx_stride (>= k, else TOPK_EINVAL)
+ *      entries apart, 4-byte aligned.  Entries are raw positions in the
+ *      row's window; any value is allowed: -1, positions at or past the
+ *      window end and duplicates are ignored or harmless.  The guess reads
+ *      the first min(k, workgroup size) entries of a hint row (256 to 1024;
+ *      keep the hints of a row in no particular order, e.g. as a selection
+ *      returns them).  NULL = no hints (the calls then equal topk_decode_v /
+ *      topk_decode_varlen).
+ * The result is the same exact selection as without hints, whatever the
+ * hints hold.  Hints whose scores give no usable bracket (all invalid, all
+ * one position, none above the sample's minimum) fall back to the sample. */
+int topk_decode_hinted(const float* logits, int64_t row_stride, const int32_t* n_valid,
+                       const int32_t* pre_idx, int64_t pre_idx_stride, int32_t num_rows, int32_t k,
+                       int32_t* indices, float* values, uint32_t flags, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
+
+int topk_decode_varlen_hinted(const float* logits, int64_t row_stride, const int32_t* kv_lens,
+                              const int32_t* pre_idx, int64_t pre_idx_stride, int32_t num_rows,
+                              int32_t next_n, int32_t compress_ratio, int32_t k, int32_t* indices,
+                              float* values, uint32_t flags, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
 /* Bytes of workspace a call with num_rows rows of stride `max_row_len` needs
  * (pass the row_stride of the call; 0 when the plan uses one workgroup per
  * row and needs none).  The value does not depend on the device.  Returns 0
@@ -161,17 +189,19 @@ const char* topk_strerror(int status);
  *      exact radix rescue runs on every long row.
  *  row_stats: optional device int32[num_rows][TOPK_STATS_WORDS]; per row:
  *      [0] path (0 short, 1 bracket + refine, 2 rescue: invalid bracket,
- *          3 rescue: crowded crossing region -- the crossing bin over the
- *          candidate cap, or (split rows) a sample predicting it -- and
- *          4 split row finished by one workgroup from memory because its
- *          candidate list missed the sample's prediction),
+ *          3 rescue: crossing bin over the candidate cap (one-workgroup
+ *          rows: also counts above the hint floor short of k), 4 rescue:
+ *          split row whose counts above its floor fell short of k),
  *      [1] m (crossing-bin population, -1 if not computed),
  *      [2] above (count in bins above the crossing bin, -1 if none),
  *      [3] crossing bin index (-1 if none),
- *      [4] bit pattern of the sample minimum, [5] of the sample maximum,
- *      [6] workgroups per row, [7] candidate cap.
+ *      [4] bit pattern of the bracket's low end (the sample minimum, or the
+ *          lowest hint score when hints steered it), [5] of its high end,
+ *      [6] workgroups per row, [7] candidate cap,
+ *      [8] split rows: the floor bin the row's histogram counts from (-1 for
+ *          one-workgroup rows and rows without a valid bracket).
  */
-#define TOPK_STATS_WORDS 8
+#define TOPK_STATS_WORDS 9
 
 typedef struct topk_options {
   int32_t force_wgs_per_row;
@@ -179,6 +209,9 @@ typedef struct topk_options {
   int32_t* row_stats;
   float* values;   /* as in topk_decode_v */
   uint32_t flags;  /* as in topk_decode_v */
+  const int32_t* pre_idx; /* as in topk_decode_hinted (decode forms only,
+                             else TOPK_EINVAL) */
+  int64_t pre_idx_stride;
 } topk_options;
 
 int topk_decode_ex(const float* logits, int64_t row_stride, const int32_t* n_valid,

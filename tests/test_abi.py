@@ -158,7 +158,20 @@ def test_output_options_and_varlen_validation():
                              None) == ert.TOPK_ELAYOUT
     assert lib.topk_prefill_v(P16, 4096, P16, P16, 4, 512, P16, None, 8, 0, None, 0,
                               None) == ert.TOPK_EINVAL
+    # hints: a stride below k, a misaligned hint array, hints on the prefill
+    # form -- all rejected on the host
+    assert lib.topk_decode_hinted(P16, 4096, P16, P16, 511, 4, 512, P16, None, 0, None, 0,
+                                  None) == ert.TOPK_EINVAL
+    assert lib.topk_decode_hinted(P16, 4096, P16, P16 + 2, 512, 4, 512, P16, None, 0, None, 0,
+                                  None) == ert.TOPK_ELAYOUT
+    assert lib.topk_decode_varlen_hinted(P16, 4096, P16, P16, 100, 4, 2, 4, 1024, P16, None, 0,
+                                         None, 0, None) == ert.TOPK_EINVAL
+    o = ert._Options(0, 0, None, None, 0, P16, 512)
+    assert lib.topk_prefill_ex(P16, 4096, P16, P16, 4, 512, P16, 0, None, 0, None,
+                               ctypes.pointer(o)) == ert.TOPK_EINVAL
     # empty batches are a no-op for every form
     assert lib.topk_decode_varlen(None, 4096, None, 0, 2, 4, 512, None, None, 0, None, 0,
                                   None) == 0
+    assert lib.topk_decode_varlen_hinted(None, 4096, None, None, 0, 0, 2, 4, 512, None, None, 0,
+                                         None, 0, None) == 0
     assert _validate(stride=1 << 30) == ert.TOPK_EINVAL

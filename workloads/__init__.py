@@ -145,6 +145,56 @@ def decode_varlen(rows: int = 64, stride: int = 131072, k: int = 2048,
 
 
 # --------------------------------------------------------------------------
+# Hinted decode step: workload 2's shape with the previous step's top-K.
+# --------------------------------------------------------------------------
+def decode_step(rows: int = 64, stride: int = 131072, k: int = 2048, lo: int = 8192,
+                hi: int = 131072, rho: float = 0.96, cfg: int = 6,
+                forced: Optional[dict] = None):
+    """A decode step and the previous step's top-K positions as hints.
+
+    Built by construction, without any selection: per long row, a random set
+    H of k positions is the previous step's top-K -- its previous scores are
+    drawn from the N(0, 1) tail above the 1 - k/n quantile (inverse CDF of a
+    uniform on that tail), the other positions' from below it -- and the
+    current scores are rho * previous + sqrt(1 - rho^2) * fresh N(0, 1),
+    times 4 (workload 2's N(0, 4) scale, without its ramp, which would move
+    the top-K away from H).  rho = 0.96 puts the overlap of H with the
+    current top-K near the 0.77 the pages report for raw hints on real
+    decode captures.  Short rows' hints are their own output (identity, then
+    -1).  Returns (Workload, hints int32 [rows, k] in random order)."""
+    from scipy.special import ndtri
+
+    if forced is None:
+        forced = {r: v for r, v in DECODE_VARLEN_FORCED.items() if r < rows}
+    x = np.empty((rows, stride), dtype=np.float32)
+    nv = np.empty(rows, dtype=np.int32)
+    hints = np.full((rows, k), -1, dtype=np.int32)
+    c = float(np.sqrt(1.0 - rho * rho))
+    for r in range(rows):
+        g = row_rng(cfg, r)
+        n_r = int(g.integers(lo, hi, endpoint=True))
+        if r in forced:
+            n_r = int(forced[r])
+        nv[r] = n_r
+        row = np.zeros(stride, dtype=np.float64)
+        if n_r > k:
+            q = 1.0 - k / n_r
+            h = g.choice(n_r, size=k, replace=False)
+            prev = ndtri(g.uniform(1e-12, q, size=n_r))
+            prev[h] = ndtri(g.uniform(q, 1.0, size=k))
+            row[:n_r] = 4.0 * (rho * prev + c * g.standard_normal(n_r))
+            hints[r] = h.astype(np.int32)
+        else:
+            row[:n_r] = 4.0 * g.standard_normal(n_r)
+            hints[r, :n_r] = np.arange(n_r, dtype=np.int32)
+        row = row.astype(np.float32)
+        _poison_row_outside(row, 0, n_r, POISON_DECODE)
+        x[r] = row
+    w = Workload(f"decode_step_hinted_{rows}x{stride}_k{k}", "decode", x, k, n_valid=nv)
+    return w, hints
+
+
+# --------------------------------------------------------------------------
 # Workload 3: prefill packed causal tile, 4 x 1024 rows, stride 16640, K=1024.
 # --------------------------------------------------------------------------
 PREFILL_OFFSETS = (0, 65, 130, 195)
