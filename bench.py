@@ -37,7 +37,8 @@ METRIC = "top-K rows/s + achieved HBM GB/s vs peak; p50/p99 µs/row, K=512..2048
 PEAK_HBM_GBS = 8000.0  # MI355X published HBM3E bandwidth
 ROTATE_BYTES = 1 << 30
 KERNEL_SOURCES = ("exact_row_top_amd/csrc/gvr_kernels.hip", "exact_row_top_amd/csrc/gvr_common.h",
-                  "exact_row_top_amd/csrc/row_window.h")
+                  "exact_row_top_amd/csrc/gvr_device.h", "exact_row_top_amd/csrc/row_window.h",
+                  "exact_row_top_amd/csrc/blockskip.hip")
 
 
 def log(*a):
@@ -113,6 +114,10 @@ def main():
                          "step with the previous step's top-K as hints")
     ap.add_argument("--no-hints", action="store_true",
                     help="workload 6 without its hints (the same rows, sample-only guess)")
+    ap.add_argument("--blockskip", type=int, default=0, choices=(-1, 0, 1),
+                    help="workloads 7 / 8 (a 128 MiB decode batch with block maxima, rows "
+                         "with locality / i.i.d.): 0 = the size gate decides, 1 = force the "
+                         "block-skip pass, -1 = the ordinary path")
     ap.add_argument("--bs", type=int, default=1, help="batch size for workload 4")
     ap.add_argument("--warm", action="store_true", help="no rotation: inputs stay cache-resident")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline leg")
@@ -139,7 +144,10 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     ert.load_library()
     hints = None
-    if args.workload == 6:
+    bsk = args.workload in (7, 8)
+    if bsk:
+        w = workloads.decode_blockskip(smooth=2.0 if args.workload == 7 else 0.0)
+    elif args.workload == 6:
         w, hints = workloads.decode_step()
         if args.no_hints:
             hints = None
@@ -162,6 +170,12 @@ def main():
         if hints is not None:
             dev_h = torch.from_numpy(hints).cuda()
             fn = lambda *a, **kw: ert.topk_decode(*a, pre_idx=dev_h, **kw)  # noqa: E731
+        if bsk:
+            # the block maxima come with the scores (the indexer GEMM's
+            # epilogue writes them); produced here once, outside the timing
+            dev_b = ert.block_max(dev_x)
+            fn = lambda *a, **kw: ert.topk_decode(*a, bmax=dev_b, blockskip=args.blockskip,  # noqa: E731
+                                                  **kw)
     else:
         ext = (torch.from_numpy(w.row_starts).cuda(), torch.from_numpy(w.row_ends).cuda())
         fn = ert.topk_prefill
@@ -171,6 +185,25 @@ def main():
     out = torch.empty((rows, k), dtype=torch.int32, device="cuda")
     ws = ert.new_workspace(rows, w.row_stride, k)
     torch.cuda.synchronize()
+    bsk_info = None
+    if bsk:
+        st = torch.full((rows, ert.STATS_WORDS), -7, dtype=torch.int32, device="cuda")
+        fn(dev_x, *ext, k, indices=out, workspace=ws, row_stats=st)
+        torch.cuda.synchronize()
+        st = st.cpu().numpy()
+        nvr = w.valid_lengths()
+        longr = nvr > k
+        nbr = (nvr + 31) // 32
+        took = bool(np.all(st[longr, 6] == 1) and np.all(st[longr, 8] > 0))
+        if took:
+            visited = int(st[longr, 8].sum())
+            # what the pass must move: the block maxima and the visited blocks
+            # of long rows, the output and the extents
+            alg_bytes = (4 * int(nbr[longr].sum()) + 128 * visited + 4 * k * rows + 4 * rows)
+            bsk_info = {"blocks_visited": visited, "blocks": int(nbr[longr].sum()),
+                        "row_bytes_per_launch": w.algorithmic_bytes()}
+        else:
+            bsk_info = {"path": "ordinary"}
     log(f"[bench] {ncopies} rotating copies ({ncopies * copy_bytes / 2**20:.0f} MiB)")
 
     def step(i):
@@ -261,6 +294,7 @@ def main():
             "cache": "warm" if args.warm else f"cold (rotating {ncopies} copies)",
             "parallelism": "single GPU",
         },
+        **({"blockskip": bsk_info} if bsk_info is not None else {}),
         "p50_us_per_row": float(np.percentile(per, 50)) / rows,
         "p99_us_per_row": float(np.percentile(per, 99)) / rows,
         "p50_us_per_launch": float(np.percentile(per, 50)),
@@ -273,7 +307,8 @@ def main():
             "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBS,
             "traffic": traffic,
-            "kernel": "gvr_topk_kernel",
+            "kernel": ("topk_blockskip_kernel" if bsk_info and "blocks_visited" in bsk_info
+                       else "gvr_topk_kernel"),
             "kernel_source_hash": kernel_hash(),
         },
     }

@@ -38,7 +38,10 @@ class _Options(ctypes.Structure):
                 ("values", ctypes.c_void_p),
                 ("flags", ctypes.c_uint32),
                 ("pre_idx", ctypes.c_void_p),
-                ("pre_idx_stride", ctypes.c_int64)]
+                ("pre_idx_stride", ctypes.c_int64),
+                ("bmax", ctypes.c_void_p),
+                ("bmax_stride", ctypes.c_int64),
+                ("blockskip", ctypes.c_int32)]
 
 
 TOPK_SORTED = 1
@@ -71,6 +74,11 @@ def load_library():
     lib.topk_decode_varlen_hinted.argtypes = [P, I64, P, P, I64, I32, I32, I32, I32, P, P,
                                               ctypes.c_uint32, P, SZ, P]
     lib.topk_decode_varlen_hinted.restype = ctypes.c_int
+    lib.topk_decode_blockskip.argtypes = [P, I64, P, P, I64, I32, I32, P, P, ctypes.c_uint32, P,
+                                          SZ, P]
+    lib.topk_decode_blockskip.restype = ctypes.c_int
+    lib.topk_block_max.argtypes = [P, I64, I32, P, I64, P]
+    lib.topk_block_max.restype = ctypes.c_int
     lib.topk_decode_varlen_ex.argtypes = [P, I64, P, I32, I32, I32, I32, P, P, SZ, P,
                                           ctypes.POINTER(_Options)]
     lib.topk_decode_varlen_ex.restype = ctypes.c_int
@@ -194,9 +202,10 @@ def _out(indices, rows, k, device):
     return indices
 
 
-def _opts(force_wgs_per_row, force_rescue, row_stats, rows, values=None, flags=0, hints=None):
+def _opts(force_wgs_per_row, force_rescue, row_stats, rows, values=None, flags=0, hints=None,
+          bmax=None, blockskip=0):
     import torch
-    if not (force_wgs_per_row or force_rescue or row_stats is not None):
+    if not (force_wgs_per_row or force_rescue or row_stats is not None or blockskip):
         return None
     if row_stats is not None:
         _require(row_stats, "row_stats", torch.int32, 2)
@@ -205,7 +214,8 @@ def _opts(force_wgs_per_row, force_rescue, row_stats, rows, values=None, flags=0
     o = _Options(int(force_wgs_per_row), int(bool(force_rescue)),
                  row_stats.data_ptr() if row_stats is not None else None,
                  values.data_ptr() if values is not None else None, int(flags),
-                 hints[0] if hints else None, hints[1] if hints else 0)
+                 hints[0] if hints else None, hints[1] if hints else 0,
+                 bmax[0] if bmax else None, bmax[1] if bmax else 0, int(blockskip))
     return ctypes.pointer(o)
 
 
@@ -237,6 +247,33 @@ def _hints(pre_idx, requests, k, device):
     return pre_idx.data_ptr(), int(stride)
 
 
+def _bmax(bmax, rows, row_stride, device):
+    """(pointer, stride) of a block-maxima tensor: float32 [rows, >=
+    ceil(row_stride / 32)] with unit inner stride; or None."""
+    import torch
+    if bmax is None:
+        return None
+    _require(bmax, "bmax", torch.float32, 2)
+    nb = (row_stride + 31) // 32
+    if bmax.device != device or bmax.shape[0] != rows or bmax.shape[1] < nb or bmax.stride(1) != 1:
+        raise ValueError(f"bmax must be float32 [{rows}, >= {nb}] with unit inner stride on {device}")
+    return bmax.data_ptr(), int(bmax.stride(0) if rows > 1 else bmax.shape[1])
+
+
+def block_max(logits, bmax=None, *, stream=None):
+    """Per-32-score block maxima of every row (the side input of the
+    block-skip pass): float32 [rows, ceil(row_stride / 32)]."""
+    import torch
+    rows, row_stride = _logits_layout(logits)
+    nb = (row_stride + 31) // 32
+    if bmax is None:
+        bmax = torch.empty((rows, nb), dtype=torch.float32, device=logits.device)
+    bp = _bmax(bmax, rows, row_stride, logits.device)
+    _check(load_library().topk_block_max(logits.data_ptr(), row_stride, rows, bp[0], bp[1],
+                                         _stream_ptr(stream, logits.device)))
+    return bmax
+
+
 def _flags(sorted_, deterministic):
     return (TOPK_SORTED if sorted_ else 0) | (TOPK_DETERMINISTIC if deterministic else 0)
 
@@ -249,16 +286,18 @@ def _ws(workspace):
 
 def topk_decode(logits, n_valid, k: int, indices=None, *, workspace=None, stream=None,
                 values=None, return_values: bool = False, sorted: bool = False,
-                deterministic: bool = False, pre_idx=None, force_wgs_per_row: int = 0,
-                force_rescue: bool = False, row_stats=None):
+                deterministic: bool = False, pre_idx=None, bmax=None, blockskip: int = 0,
+                force_wgs_per_row: int = 0, force_rescue: bool = False, row_stats=None):
     """Exact top-k of logits[r, :n_valid[r]] per row (local indices, -1 pad).
 
     values / return_values: also the selected scores (-FLT_MAX pad); sorted:
     long rows ordered by value descending, then index ascending;
     deterministic: the k-th value's ties resolved by smallest index; pre_idx:
     optional int32 [rows, >= k] hints (the previous step's top-k positions),
-    which steer the guess only.  Returns the indices, or (indices, values)
-    when values are asked for."""
+    which steer the guess only; bmax: optional per-32-score block maxima
+    (see block_max) for the block-skip pass, taken when the batch passes its
+    size gate (blockskip=1 forces it, -1 never).  Returns the indices, or
+    (indices, values) when values are asked for."""
     import torch
     lib = load_library()
     rows, row_stride = _logits_layout(logits)
@@ -269,12 +308,24 @@ def topk_decode(logits, n_valid, k: int, indices=None, *, workspace=None, stream
     vals = _values(values, return_values, rows, k, logits.device)
     flags = _flags(sorted, deterministic)
     hints = _hints(pre_idx, rows, k, logits.device)
+    bm = _bmax(bmax, rows, row_stride, logits.device)
     wp, wb = _ws(workspace)
-    opts = _opts(force_wgs_per_row, force_rescue, row_stats, rows, vals, flags, hints)
+    opts = _opts(force_wgs_per_row, force_rescue, row_stats, rows, vals, flags, hints, bm,
+                 blockskip)
     s = _stream_ptr(stream, logits.device)
     if opts is not None:
         rc = lib.topk_decode_ex(logits.data_ptr(), row_stride, n_valid.data_ptr(), rows, k,
                                 out.data_ptr(), wp, wb, s, opts)
+    elif bm is not None and hints is None:
+        rc = lib.topk_decode_blockskip(logits.data_ptr(), row_stride, n_valid.data_ptr(), bm[0],
+                                       bm[1], rows, k, out.data_ptr(),
+                                       vals.data_ptr() if vals is not None else None, flags, wp,
+                                       wb, s)
+    elif bm is not None:
+        o = _Options(0, 0, None, vals.data_ptr() if vals is not None else None, int(flags),
+                     hints[0], hints[1], bm[0], bm[1], 0)
+        rc = lib.topk_decode_ex(logits.data_ptr(), row_stride, n_valid.data_ptr(), rows, k,
+                                out.data_ptr(), wp, wb, s, ctypes.pointer(o))
     elif hints is not None:
         rc = lib.topk_decode_hinted(logits.data_ptr(), row_stride, n_valid.data_ptr(), hints[0],
                                     hints[1], rows, k, out.data_ptr(),
@@ -331,14 +382,14 @@ def topk_prefill(logits, row_starts, row_ends, k: int, indices=None, *, max_row_
 def topk_decode_varlen(logits, kv_lens, k: int, next_n: int = 1, compress_ratio: int = 1,
                        indices=None, *, workspace=None, stream=None, values=None,
                        return_values: bool = False, sorted: bool = False,
-                       deterministic: bool = False, pre_idx=None, force_wgs_per_row: int = 0,
-                       force_rescue: bool = False, row_stats=None):
+                       deterministic: bool = False, pre_idx=None, bmax=None, blockskip: int = 0,
+                       force_wgs_per_row: int = 0, force_rescue: bool = False, row_stats=None):
     """Exact top-k of the varlen / MTP decode form: row r selects from
     logits[r, :n] with n = (kv_lens[r // next_n] - next_n + r % next_n + 1) //
     compress_ratio (no window when kv_lens[r // next_n] < next_n), computed on
     the device from the per-request kv_lens.  pre_idx: optional int32
     [requests, >= k] hints, one row per request shared by its next_n rows.
-    Output options as for topk_decode."""
+    bmax / blockskip and the output options as for topk_decode."""
     import torch
     lib = load_library()
     rows, row_stride = _logits_layout(logits)
@@ -350,8 +401,14 @@ def topk_decode_varlen(logits, kv_lens, k: int, next_n: int = 1, compress_ratio:
     vals = _values(values, return_values, rows, k, logits.device)
     flags = _flags(sorted, deterministic)
     hints = _hints(pre_idx, need, k, logits.device)
+    bm = _bmax(bmax, rows, row_stride, logits.device)
     wp, wb = _ws(workspace)
-    opts = _opts(force_wgs_per_row, force_rescue, row_stats, rows, vals, flags, hints)
+    opts = _opts(force_wgs_per_row, force_rescue, row_stats, rows, vals, flags, hints, bm,
+                 blockskip)
+    if opts is None and bm is not None:
+        opts = ctypes.pointer(_Options(0, 0, None, vals.data_ptr() if vals is not None else None,
+                                       int(flags), hints[0] if hints else None,
+                                       hints[1] if hints else 0, bm[0], bm[1], 0))
     s = _stream_ptr(stream, logits.device)
     if opts is not None:
         rc = lib.topk_decode_varlen_ex(logits.data_ptr(), row_stride, kv_lens.data_ptr(), rows,
@@ -383,6 +440,6 @@ def new_workspace(num_rows: int, row_stride: int, k: int, device="cuda", stream=
     return ws
 
 
-__all__ = ["topk_decode", "topk_prefill", "topk_decode_varlen", "workspace_bytes", "new_workspace", "plan_query",
+__all__ = ["topk_decode", "topk_prefill", "topk_decode_varlen", "block_max", "workspace_bytes", "new_workspace", "plan_query",
            "strerror", "load_library", "TopKError", "STATS_WORDS", "VALID_K", "TOPK_SORTED",
            "TOPK_DETERMINISTIC"]

@@ -46,511 +46,14 @@
 #include <stdint.h>
 
 #include "gvr_common.h"
+#include "gvr_device.h"
 #include "row_window.h"
 
 namespace ert {
 
-typedef float f4 __attribute__((ext_vector_type(4)));
-
-// ---------------------------------------------------------------------------
-// Scalar helpers
-// ---------------------------------------------------------------------------
-
-// Order-preserving key: canonicalise -0 to +0, then flip so unsigned order
-// matches IEEE order (negatives inverted, positives get the top bit).
-__device__ __forceinline__ uint32_t fkey(float x) {
-  uint32_t b = __float_as_uint(x);
-  b = (b == 0x80000000u) ? 0u : b;
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-
-__device__ __forceinline__ float from_key(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
-}
-
-// Rescue key: fkey, with every NaN (the masked-lane marker) mapped to 0, the
-// lowest key, so it sits below -inf (key 0x007FFFFF) and is never selected
-// while the row holds K non-NaN scores.
-__device__ __forceinline__ uint32_t rkey(float x) { return (x == x) ? fkey(x) : 0u; }
-
-// The bracket's bin map: bin(x) = trunc(clamp(fma(x, sc, c0), 0, kBins - 1))
-// with sc = kBins / (gmax - gmin) and c0 = -gmin * sc, each rounded once per
-// row.  A fused multiply-add is monotone non-decreasing in x, so equal values
-// share a bin and bins ascend with the value; this is the single definition
-// every step uses.  The same map scaled by 4 (exact: a power-of-two scale)
-// gives a bin's LDS byte offset directly.  The final masks only matter for
-// NaN (outside the contract): they keep the LDS index in range.
-struct BinMap {
-  float gmin, sc, c0, sc4, c04;
-};
-__device__ __forceinline__ int vbin(float x, const BinMap& bm) {
-  float t = __builtin_fmaf(x, bm.sc, bm.c0);
-  t = __builtin_amdgcn_fmed3f(t, 0.0f, (float)(kBins - 1));
-  return ((int)t) & (kBins - 1);
-}
-__device__ __forceinline__ uint32_t vbin_off(float x, const BinMap& bm) {
-  float t = __builtin_fmaf(x, bm.sc4, bm.c04);
-  t = __builtin_amdgcn_fmed3f(t, 0.0f, (float)(4 * (kBins - 1)));
-  return ((uint32_t)(int)t) & (uint32_t)(4 * kBins - 4);
-}
-// LDS histogram word at a byte offset from vbin_off.
-__device__ __forceinline__ uint32_t* hword(uint32_t* h, uint32_t off) {
-  return reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(h) + off);
-}
-
-__device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
-
-__device__ __forceinline__ uint32_t atomic_add_agent(uint32_t* p, uint32_t v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void atomic_add_agent_nr(uint32_t* p, uint32_t v) {
-  (void)__hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Wait until this wave's vector memory operations (stores, atomics) have
-// completed: s_waitcnt vmcnt(0) (gfx9 encoding: expcnt and lgkmcnt fields at
-// their no-wait maxima).  Every wave runs it before the workgroup barrier
-// that precedes one thread's release and arrival, so what all waves wrote is
-// performed before any other workgroup can see the arrival.
-__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-__device__ __forceinline__ uint32_t load_agent(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void lds_inc(uint32_t* p) {
-  __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-__device__ __forceinline__ uint32_t lds_take(uint32_t* p) {
-  return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-
-// Count one per lane with `act` into h[d]; when every such lane of the wave
-// has the same d (tie-heavy rows), one lane adds them all at once instead of
-// 64 conflicting increments.  The first lane's d comes from readfirstlane
-// (no LDS round trip).  Must be reached by the whole wave.
-__device__ __forceinline__ void lds_inc_agg(uint32_t* h, uint32_t d, bool act) {
-  if (act) {
-    const uint32_t d0 = __builtin_amdgcn_readfirstlane(d);
-    const uint64_t am = __ballot(1);
-    const uint64_t same = __ballot(d == d0);
-    if (same == am) {
-      if ((uint32_t)lane_id() == (uint32_t)(__ffsll((unsigned long long)am) - 1))
-        __hip_atomic_fetch_add(&h[d0], (uint32_t)__popcll(am), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_WORKGROUP);
-    } else {
-      __hip_atomic_fetch_add(&h[d], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    }
-  }
-}
-
-// Append the lanes with `pred` to an LDS-counted list: one atomic per wave,
-// lane order inside the wave.  Returns each predicated lane's position.
-// Must be reached by the whole wave.
-__device__ __forceinline__ uint32_t wave_append(bool pred, uint32_t* ctr) {
-  const uint64_t m = __ballot(pred);
-  uint32_t base = 0;
-  if (m != 0ull) {
-    const int leader = __ffsll((unsigned long long)m) - 1;
-    if (lane_id() == leader)
-      base = __hip_atomic_fetch_add(ctr, (uint32_t)__popcll(m), __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_WORKGROUP);
-    base = __shfl(base, leader, 64);
-  }
-  const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-  return base + below;
-}
-
-// Rank-count selection of the `need` largest among m <= kRankMax candidates
-// held in LDS (key[], idx[]): a candidate's rank is the number with a larger
-// key, or an equal key and a smaller index; ranks below `need` go to
-// out[base + rank] (value descending, smallest index first inside a tie).
-// The arrays are padded to a multiple of 4 with keys that rank nothing.
-template <int BLOCK>
-__device__ __forceinline__ void rank_select(uint32_t* key, int32_t* idx, uint32_t m, uint32_t need,
-                                            int32_t* out, uint32_t base) {
-  const int t = threadIdx.x;
-  const uint32_t m4 = (m + 3u) & ~3u;
-  if ((uint32_t)t >= m && (uint32_t)t < m4) {
-    key[t] = 0u;
-    idx[t] = 0x7FFFFFFF;
-  }
-  __syncthreads();
-  if ((uint32_t)t < m) {
-    const uint32_t kk = key[t];
-    const int32_t ii = idx[t];
-    uint32_t rank = 0;
-    for (uint32_t j = 0; j < m4; j += 4) {
-      const uint4 kj = *reinterpret_cast<const uint4*>(key + j);
-      const int4 ij = *reinterpret_cast<const int4*>(idx + j);
-      rank += (kj.x > kk || (kj.x == kk && ij.x < ii)) ? 1u : 0u;
-      rank += (kj.y > kk || (kj.y == kk && ij.y < ii)) ? 1u : 0u;
-      rank += (kj.z > kk || (kj.z == kk && ij.z < ii)) ? 1u : 0u;
-      rank += (kj.w > kk || (kj.w == kk && ij.w < ii)) ? 1u : 0u;
-    }
-    if (rank < need) out[base + rank] = ii;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Wave and block primitives
-// ---------------------------------------------------------------------------
-
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
-}
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-
-// Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts
-// (within rows of 16) and the gfx9 row broadcasts (across rows).
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  const int l = lane_id();
-  const int rl = l & 15;
-  uint32_t s;
-  s = dpp_u32<0x111>(v);
-  v += (rl >= 1) ? s : 0u;
-  s = dpp_u32<0x112>(v);
-  v += (rl >= 2) ? s : 0u;
-  s = dpp_u32<0x114>(v);
-  v += (rl >= 4) ? s : 0u;
-  s = dpp_u32<0x118>(v);
-  v += (rl >= 8) ? s : 0u;
-  s = dpp_u32<0x142>(v);
-  v += ((l & 31) >= 16) ? s : 0u;
-  s = dpp_u32<0x143>(v);
-  v += (l >= 32) ? s : 0u;
-  return v;
-}
-
-// Min and max over a wave (result in every lane, read from lane 63).  NaN
-// inputs are ignored by fminf / fmaxf.
-__device__ __forceinline__ void wave_minmax(float& mn, float& mx) {
-  const int l = lane_id();
-  const int rl = l & 15;
-  float a, b;
-#define ERT_STEP(CTRL, COND) \
-  a = dpp_f32<CTRL>(mn);     \
-  b = dpp_f32<CTRL>(mx);     \
-  if (COND) {                \
-    mn = fminf(mn, a);       \
-    mx = fmaxf(mx, b);       \
-  }
-  ERT_STEP(0x111, rl >= 1)
-  ERT_STEP(0x112, rl >= 2)
-  ERT_STEP(0x114, rl >= 4)
-  ERT_STEP(0x118, rl >= 8)
-  ERT_STEP(0x142, (l & 31) >= 16)
-  ERT_STEP(0x143, l >= 32)
-#undef ERT_STEP
-  mn = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mn), 63));
-  mx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mx), 63));
-}
-
-// Exclusive prefix sum over the block in thread order; `total` gets the sum.
-// `sm` holds BLOCK/64 words.  Contains two __syncthreads.
-// Exclusive offsets of v over the whole workgroup in an arbitrary wave order:
-// a wave prefix sum and one LDS add per wave on *ctr (zero beforehand).  No
-// workgroup barrier.  Must be reached by the whole wave.
-__device__ __forceinline__ uint32_t wave_offsets(uint32_t v, uint32_t* ctr) {
-  const uint32_t inc = wave_incl_scan(v);
-  uint32_t base = 0u;
-  if (lane_id() == 63)
-    base = __hip_atomic_fetch_add(ctr, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  base = (uint32_t)__builtin_amdgcn_readlane((int)base, 63);
-  return base + inc - v;
-}
-
-template <int BLOCK>
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sm, uint32_t& total) {
-  constexpr int W = BLOCK / 64;
-  const uint32_t inc = wave_incl_scan(v);
-  const int w = threadIdx.x >> 6;
-  if (lane_id() == 63) sm[w] = inc;
-  __syncthreads();
-  uint32_t off = 0, tot = 0;
-#pragma unroll
-  for (int i = 0; i < W; ++i) {
-    const uint32_t s = sm[i];
-    off += (i < w) ? s : 0u;
-    tot += s;
-  }
-  __syncthreads();
-  total = tot;
-  return off + inc - v;
-}
-
-struct Cross {
-  int b;           // crossing bin / digit, -1 if the total is below target
-  uint32_t above;  // count strictly above it
-  uint32_t m;      // count inside it
-  uint32_t total;
-};
-
-// The crossing that find_crossing left in LDS, held in scalar registers (every
-// lane reads the same words; readfirstlane keeps them out of the VGPR budget
-// the resident row needs).
-__device__ __forceinline__ Cross read_cross(const Cross* c) {
-  Cross r;
-  r.b = __builtin_amdgcn_readfirstlane(c->b);
-  r.above = __builtin_amdgcn_readfirstlane(c->above);
-  r.m = __builtin_amdgcn_readfirstlane(c->m);
-  r.total = __builtin_amdgcn_readfirstlane(c->total);
-  return r;
-}
-
-// Find the highest bin b with sum_{b' >= b} h[b'] >= target over NBINS bins,
-// where load(b) returns h[b].  Thread t owns PER consecutive bins from the
-// top.  Result in *out (LDS), visible to all threads on return.
-template <int NBINS, int BLOCK, class Load>
-__device__ __forceinline__ void find_crossing(Load&& load, uint32_t target, Cross* out,
-                                              uint32_t* scan_sm) {
-  constexpr int PER = NBINS >= BLOCK ? NBINS / BLOCK : 1;
-  constexpr int OWNERS = NBINS / PER;
-  static_assert(PER * OWNERS == NBINS, "bins per thread");
-  const int t = threadIdx.x;
-  const int hi = NBINS - 1 - t * PER;
-  uint32_t c[PER];
-  uint32_t s = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    c[i] = (t < OWNERS) ? load(hi - i) : 0u;
-    s += c[i];
-  }
-  uint32_t tot;
-  const uint32_t ex = block_excl_scan<BLOCK>(s, scan_sm, tot);
-  if (t < OWNERS && ex < target && ex + s >= target) {
-    uint32_t run = ex;
-    bool found = false;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      if (!found && run + c[i] >= target) {
-        out->b = hi - i;
-        out->above = run;
-        out->m = c[i];
-        out->total = tot;
-        found = true;
-      }
-      run += c[i];
-    }
-  }
-  if (t == 0 && tot < target) {
-    out->b = -1;
-    out->above = tot;
-    out->m = 0;
-    out->total = tot;
-  }
-  __syncthreads();
-}
-
-// Smallest score x (IEEE order over [-inf, +inf]) with vbin(x) >= b, so that
-// for every non-NaN x: vbin(x) >= b  <=>  x >= edge.  vbin is monotone in x,
-// so the set is an up-set.  The 64 lanes first probe the keys around the
-// arithmetic estimate gmin + b / sc (rounding puts the edge within a few
-// ulps of it); if the edge is not among them, a 64-way search over the keys
-// of -inf .. +inf (six rounds) finds it.  b <= 0 gives -inf; b >= kBins gives
-// NaN, which no score compares >= to.  Must be called by a whole wave.
-__device__ __forceinline__ float bin_edge(int b, const BinMap& bm) {
-  if (b <= 0) return -__builtin_inff();
-  if (b >= kBins) return __builtin_nanf("");
-  uint32_t lo = 0x007FFFFFu;  // key(-inf): vbin = 0 < b
-  uint32_t hi = 0xFF800000u;  // key(+inf): vbin = kBins - 1 >= b
-  const uint32_t l = (uint32_t)lane_id();
-  {
-    const float est = bm.gmin + (float)b / bm.sc;
-    const uint32_t c = fkey(est);
-    const int64_t pk = (int64_t)c - 31 + (int64_t)l;
-    const uint32_t probe =
-        pk < (int64_t)lo ? lo : (pk > (int64_t)hi ? hi : (uint32_t)pk);
-    const bool ok = vbin(from_key(probe), bm) >= b;
-    const uint64_t mask = __ballot(ok);
-    if (mask != 0ull && (mask & 1ull) == 0ull) {
-      // the first passing lane is the edge unless probes were clamped
-      const int f = __ffsll((unsigned long long)mask) - 1;
-      const uint32_t e = (uint32_t)__builtin_amdgcn_readlane((int)probe, f);
-      const uint32_t below = (uint32_t)__builtin_amdgcn_readlane((int)probe, f - 1);
-      if (below + 1u == e) return from_key(e);
-      lo = below;
-      hi = e;
-    } else if (mask == 0ull) {
-      lo = (uint32_t)__builtin_amdgcn_readlane((int)probe, 63);
-    } else {
-      hi = (uint32_t)__builtin_amdgcn_readlane((int)probe, 0);
-    }
-  }
-  while (hi - lo > 1u) {
-    const uint32_t span = hi - lo;
-    const uint32_t step = span / 64u + ((span & 63u) ? 1u : 0u);
-    const uint64_t pk = (uint64_t)lo + (uint64_t)(l + 1u) * step;
-    const uint32_t probe = pk >= (uint64_t)hi ? hi : (uint32_t)pk;
-    const bool ok = vbin(from_key(probe), bm) >= b;
-    const uint64_t mask = __ballot(ok);  // lane 63 probes hi, so mask != 0
-    const int f = __ffsll((unsigned long long)mask) - 1;
-    const uint32_t nhi = (uint32_t)__builtin_amdgcn_readlane((int)probe, f);
-    const uint32_t nlo = (f > 0) ? (uint32_t)__builtin_amdgcn_readlane((int)probe, f - 1) : lo;
-    lo = nlo;
-    hi = nhi;
-  }
-  return from_key(hi);
-}
-
-
-// Barrier over the G workgroups of one row (split tier).  Arrivals add one
-// to the slot's counter, which only the row's last finishing workgroup
-// returns to zero, so a workgroup's n-th barrier is passed once the counter
-// reaches n * G (`nbar` counts this workgroup's barriers).  Everything that
-// crosses between workgroups is an agent-scope atomic (adds, loads, stores),
-// so no cache write-back or invalidate is needed: each wave only waits for
-// its own atomics to complete before the workgroup arrives.  Spins are
-// bounded: on timeout an error flag is raised in the workspace and the
-// workgroup moves on (results are then undefined, but every wave exits).
-__device__ __forceinline__ void row_barrier(SlotHeader* hdr, int G, uint32_t& nbar, uint32_t* err) {
-  wait_vm();
-  __syncthreads();
-  ++nbar;
-  if (threadIdx.x == 0) {
-    atomic_add_agent_nr(&hdr->bar_count, 1u);
-    const uint32_t target = nbar * (uint32_t)G;
-    uint32_t spins = 0;
-    while (load_agent(&hdr->bar_count) < target) {
-      __builtin_amdgcn_s_sleep(1);
-      if (++spins > (1u << 24)) {
-        atomic_add_agent_nr(err, kErrBarrierTimeout);
-        break;
-      }
-    }
-  }
-  __syncthreads();
-}
-
-// Count this workgroup as done with its row's slot; true in the last one.
-// What the others wrote for it (list entries, counters) are agent-scope
-// atomics they completed before counting themselves.
-__device__ __forceinline__ bool finish_slot(SlotHeader* hdr, int G, uint32_t* bc) {
-  wait_vm();
-  __syncthreads();
-  if (threadIdx.x == 0) *bc = atomic_add_agent(&hdr->done, 1u);
-  __syncthreads();
-  return *bc == (uint32_t)(G - 1);
-}
-
-__device__ __forceinline__ void rest_slot(SlotFixed* sf, int t, int block) {
-  for (int i = t; i < 8 * 256; i += block) (&sf->dig[0][0])[i] = 0u;
-  for (int i = t; i < kBins; i += block) sf->hist[i] = 0u;
-  if (t == 0) {
-    sf->hdr.bar_count = 0u;
-    sf->hdr.win_cur = 0u;
-    sf->hdr.cand_cur = 0u;
-    sf->hdr.tie_cur = 0u;
-    sf->hdr.done = 0u;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Exact radix selection over an element set
-// ---------------------------------------------------------------------------
-
-struct RSel {
-  uint32_t thr;    // key >> shift of the threshold digit path
-  int shift;       // 24, 16, 8 or 0
-  uint32_t rem;    // how many of the elements with key >> shift == thr to take
-  uint32_t cnt;    // how many elements have key >> shift == thr
-};
-
-// The `need` largest keys among the elements `iter` visits (iter(f) calls
-// f(key) for each element this thread owns): up to four 8-bit digit levels
-// from the top, stopping early when the crossing digit's members are all
-// needed.  Afterwards an element is selected iff key >> shift > thr, or
-// key >> shift == thr and it is one of `rem` such elements.  With `gdig`
-// (split rescue) the digit counts of the row's G workgroups are summed
-// through the workspace behind a barrier at each level.
-template <int BLOCK, bool AGG = false, class Iter>
-__device__ __forceinline__ RSel radix_select(Iter&& iter, uint32_t need, uint32_t* dh, Cross* cross,
-                                             uint32_t* scan, uint32_t* gdig, SlotHeader* hdr, int G,
-                                             uint32_t& nbar, uint32_t* err) {
-  const int t = threadIdx.x;
-  uint32_t prefix = 0, rem = need, cnt = 0;
-  int shift = 24;
-  for (int L = 0; L < 4; ++L) {
-    shift = 24 - 8 * L;
-    for (int i = t; i < 256; i += BLOCK) dh[i] = 0u;
-    __syncthreads();
-    iter([&](uint32_t key) {
-      const bool act = L == 0 || ((key ^ prefix) >> (shift + 8)) == 0u;
-      if (AGG)
-        lds_inc_agg(dh, (key >> shift) & 255u, act);
-      else if (act)
-        lds_inc(&dh[(key >> shift) & 255u]);
-    });
-    __syncthreads();
-    if (gdig) {
-      uint32_t* gd = gdig + L * 256;
-      for (int i = t; i < 256; i += BLOCK) {
-        const uint32_t c = dh[i];
-        if (c) atomic_add_agent(&gd[i], c);
-      }
-      row_barrier(hdr, G, nbar, err);
-      find_crossing<256, BLOCK>([&](int d) { return load_agent(&gd[d]); }, rem, cross, scan);
-    } else {
-      find_crossing<256, BLOCK>([&](int d) { return dh[d]; }, rem, cross, scan);
-    }
-    const Cross c = read_cross(cross);
-    prefix |= (uint32_t)c.b << shift;
-    rem -= c.above;
-    cnt = c.m;
-    if (c.m == rem) break;
-  }
-  return RSel{prefix >> shift, shift, rem, cnt};
-}
-
-// The `need` largest of the m (key, index) pairs held in LDS, written from
-// out[base] on (those in the K-th key's digit class after the others): an
-// 8-bit radix select over the keys.  With `det`, when the K-th key's class
-// holds more members than are needed, a second radix select over the
-// complemented indices of that class (non-members count as key 0) keeps the
-// smallest indices: that class then always ends with every member of its last
-// digit needed, so the choice involves no ticket.  `ctr` is two LDS words,
-// zero on entry.
-template <int BLOCK>
-__device__ __forceinline__ void list_select(const uint32_t* key, const int32_t* idx, uint32_t m,
-                                            uint32_t need, bool det, int32_t* out, uint32_t base,
-                                            uint32_t limit, uint32_t* dh, Cross* cross,
-                                            uint32_t* scan, uint32_t* ctr, uint32_t& nbar) {
-  const int t = threadIdx.x;
-  const RSel s = radix_select<BLOCK>(
-      [&](auto&& f) {
-        for (uint32_t i = t; i < m; i += BLOCK) f(key[i]);
-      },
-      need, dh, cross, scan, nullptr, nullptr, 1, nbar, nullptr);
-  const bool pick = det && s.cnt > s.rem;
-  RSel s2{0u, 0, 0u, 0u};
-  if (pick) {
-    const uint32_t tk = s.thr;  // the loop ran all four levels: one exact key
-    s2 = radix_select<BLOCK>(
-        [&](auto&& f) {
-          for (uint32_t i = t; i < m; i += BLOCK) f(key[i] == tk ? ~(uint32_t)idx[i] : 0u);
-        },
-        s.rem, dh, cross, scan, nullptr, nullptr, 1, nbar, nullptr);
-  }
-  const uint32_t eq_base = base + (need - s.rem);
-  for (uint32_t i = t; i < m; i += BLOCK) {
-    const uint32_t d = key[i] >> s.shift;
-    if (d > s.thr) {
-      const uint32_t pos = base + lds_take(&ctr[0]);
-      if (pos < limit) out[pos] = idx[i];
-    } else if (d == s.thr && (!pick || ((~(uint32_t)idx[i]) >> s2.shift) >= s2.thr)) {
-      const uint32_t tk = lds_take(&ctr[1]);
-      if (tk < s.rem && eq_base + tk < limit) out[eq_base + tk] = idx[i];
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
 // The kernel
 // ---------------------------------------------------------------------------
-
-constexpr int kRankMax = 256;  // refine by rank counting up to this many candidates
 
 template <int BLOCK>
 struct alignas(16) Smem {

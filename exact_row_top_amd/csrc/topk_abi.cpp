@@ -14,6 +14,8 @@
 namespace ert {
 const void* gvr_kernel(int k, int block, int qpt, bool split);
 const void* epilogue_kernel(int k);
+const void* blockskip_kernel(int k);
+const void* block_max_kernel_ptr();
 }
 
 using namespace ert;
@@ -214,6 +216,44 @@ int device_info(DevInfo** out, int* dev_out) {
   return TOPK_OK;
 }
 
+// Shape-only gate of the block-skip pass (PR 18122 "Description"): the batch's
+// padded working set reaches 128 MiB and rows are long against K (the row
+// stride stands for the row length: no data-dependent term).
+bool blockskip_gate(int32_t num_rows, int64_t row_stride, int32_t k) {
+  return (int64_t)num_rows * row_stride * 4 >= ((int64_t)128 << 20) && row_stride >= (int64_t)72 * k;
+}
+
+// Output stage after the selection: values and / or sorted long rows.
+int launch_epilogue(const GvrParams& prm, int32_t k, int32_t num_rows, float* values,
+                    uint32_t flags, hipStream_t stream) {
+  if (values || (flags & TOPK_SORTED)) {
+    // output stage: values and / or sorted long rows, one workgroup per row
+    const void* epi = epilogue_kernel(k);
+    if (!epi) return TOPK_EINVAL;
+    EpiParams ep;
+    memset(&ep, 0, sizeof(ep));
+    ep.logits = prm.logits;
+    ep.row_stride = prm.row_stride;
+    ep.n_valid = prm.n_valid;
+    ep.row_starts = prm.row_starts;
+    ep.row_ends = prm.row_ends;
+    ep.varlen = prm.varlen;
+    ep.sorted = (flags & TOPK_SORTED) ? 1 : 0;
+    ep.indices = prm.indices;
+    ep.values = values;
+    constexpr int64_t kMaxGrid = (int64_t)1 << 30;
+    for (int64_t r0 = 0; r0 < num_rows; r0 += kMaxGrid) {
+      const int64_t nr = (num_rows - r0) < kMaxGrid ? (num_rows - r0) : kMaxGrid;
+      ep.row_begin = (int32_t)r0;
+      void* args[] = {&ep};
+      if (hipLaunchKernel(epi, dim3((unsigned)nr), dim3(kEpiBlock), args, 0, stream) != hipSuccess)
+        return TOPK_ELAUNCH;
+    }
+  }
+  if (hipGetLastError() != hipSuccess) return TOPK_ELAUNCH;
+  return TOPK_OK;
+}
+
 int run(int mode, const float* logits, int64_t row_stride, const int32_t* e1, const int32_t* e2,
         int32_t num_rows, int32_t k, int32_t* indices, int64_t max_row_len, void* workspace,
         size_t workspace_bytes, hipStream_t stream, const topk_options* opts,
@@ -233,6 +273,16 @@ int run(int mode, const float* logits, int64_t row_stride, const int32_t* e1, co
     if (opts->pre_idx_stride < k) return TOPK_EINVAL;
     if (!aligned(hints, 4)) return TOPK_ELAYOUT;
   }
+  const float* bmax = opts ? opts->bmax : nullptr;
+  const int32_t bsk_mode = opts ? opts->blockskip : 0;
+  if (bsk_mode < -1 || bsk_mode > 1) return TOPK_EINVAL;
+  if (bmax) {
+    if (mode != 0) return TOPK_EINVAL;  // block-skip serves the decode forms
+    if (opts->bmax_stride < (row_stride + 31) / 32) return TOPK_EINVAL;
+    if (!aligned(bmax, 4)) return TOPK_ELAYOUT;
+  } else if (bsk_mode == 1) {
+    return TOPK_EINVAL;  // forced block-skip needs block maxima
+  }
   if (num_rows == 0) return TOPK_OK;
   // Plans are sized for the full row stride, so any window inside it fits the
   // resident capacity; the prefill length hint is accepted but not needed.
@@ -244,6 +294,33 @@ int run(int mode, const float* logits, int64_t row_stride, const int32_t* e1, co
   int dev = 0;
   rc = device_info(&d, &dev);
   if (rc != TOPK_OK) return rc;
+
+  GvrParams prm;
+  memset(&prm, 0, sizeof(prm));
+  prm.logits = logits;
+  prm.row_stride = row_stride;
+  prm.n_valid = (mode == 0 && !vf) ? e1 : nullptr;
+  prm.row_starts = (mode == 1) ? e1 : nullptr;
+  prm.row_ends = (mode == 1) ? e2 : nullptr;
+  if (vf) prm.varlen = VarlenForm{e1, vf->next_n, vf->compress_ratio};
+  prm.force_rescue = (opts && opts->force_rescue) ? 1 : 0;
+  prm.deterministic = (flags & TOPK_DETERMINISTIC) ? 1 : 0;
+  prm.indices = indices;
+  prm.row_stats = opts ? opts->row_stats : nullptr;
+
+  if (bmax && bsk_mode >= 0 && (bsk_mode == 1 || blockskip_gate(num_rows, row_stride, k))) {
+    // block-skip pass: one 1024-thread workgroup per row, no workspace
+    const void* kern = blockskip_kernel(k);
+    if (!kern) return TOPK_EINVAL;
+    prm.wgs_per_row = 1;
+    prm.rows = num_rows;
+    prm.row_begin = 0;
+    int64_t bstride = opts->bmax_stride;
+    void* args[] = {&prm, &bmax, &bstride};
+    if (hipLaunchKernel(kern, dim3((unsigned)num_rows), dim3(1024), args, 0, stream) != hipSuccess)
+      return TOPK_ELAUNCH;
+    return launch_epilogue(prm, k, num_rows, values, flags, stream);
+  }
 
   // The plan's first guess may be for a single workgroup per row; the split
   // capacity is only consulted when G > 1.
@@ -283,23 +360,11 @@ int run(int mode, const float* logits, int64_t row_stride, const int32_t* e1, co
 
   const void* kern = gvr_kernel(k, pl.block, pl.qpt, pl.G > 1);
   if (!kern) return TOPK_EINVAL;
-  GvrParams prm;
-  memset(&prm, 0, sizeof(prm));
-  prm.logits = logits;
-  prm.row_stride = row_stride;
-  prm.n_valid = (mode == 0 && !vf) ? e1 : nullptr;
-  prm.row_starts = (mode == 1) ? e1 : nullptr;
-  prm.row_ends = (mode == 1) ? e2 : nullptr;
-  if (vf) prm.varlen = VarlenForm{e1, vf->next_n, vf->compress_ratio};
   prm.wgs_per_row = pl.G;
   prm.cap = pl.cap;
-  prm.force_rescue = (opts && opts->force_rescue) ? 1 : 0;
-  prm.deterministic = (flags & TOPK_DETERMINISTIC) ? 1 : 0;
   prm.hints = hints;
   prm.hint_stride = hints ? opts->pre_idx_stride : 0;
   prm.hint_div = vf ? vf->next_n : 1;  // hints are per request
-  prm.indices = indices;
-  prm.row_stats = opts ? opts->row_stats : nullptr;
   prm.ws = ws;
   for (int64_t r0 = 0; r0 < num_rows; r0 += pl.rows_per_launch) {
     const int64_t nr = (num_rows - r0) < pl.rows_per_launch ? (num_rows - r0) : pl.rows_per_launch;
@@ -317,32 +382,7 @@ int run(int mode, const float* logits, int64_t row_stride, const int32_t* e1, co
     if (hipLaunchKernel(kern, dim3((unsigned)grid), dim3(pl.block), args, 0, stream) != hipSuccess)
       return TOPK_ELAUNCH;
   }
-  if (values || (flags & TOPK_SORTED)) {
-    // output stage: values and / or sorted long rows, one workgroup per row
-    const void* epi = epilogue_kernel(k);
-    if (!epi) return TOPK_EINVAL;
-    EpiParams ep;
-    memset(&ep, 0, sizeof(ep));
-    ep.logits = logits;
-    ep.row_stride = row_stride;
-    ep.n_valid = prm.n_valid;
-    ep.row_starts = prm.row_starts;
-    ep.row_ends = prm.row_ends;
-    ep.varlen = prm.varlen;
-    ep.sorted = (flags & TOPK_SORTED) ? 1 : 0;
-    ep.indices = indices;
-    ep.values = values;
-    constexpr int64_t kMaxGrid = (int64_t)1 << 30;
-    for (int64_t r0 = 0; r0 < num_rows; r0 += kMaxGrid) {
-      const int64_t nr = (num_rows - r0) < kMaxGrid ? (num_rows - r0) : kMaxGrid;
-      ep.row_begin = (int32_t)r0;
-      void* args[] = {&ep};
-      if (hipLaunchKernel(epi, dim3((unsigned)nr), dim3(kEpiBlock), args, 0, stream) != hipSuccess)
-        return TOPK_ELAUNCH;
-    }
-  }
-  if (hipGetLastError() != hipSuccess) return TOPK_ELAUNCH;
-  return TOPK_OK;
+  return launch_epilogue(prm, k, num_rows, values, flags, stream);
 }
 
 }  // namespace
@@ -427,6 +467,41 @@ int topk_decode_varlen_hinted(const float* logits, int64_t row_stride, const int
   const VarlenForm vf{kv_lens, next_n, compress_ratio};
   return run(0, logits, row_stride, kv_lens, nullptr, num_rows, k, indices, 0, workspace,
              workspace_bytes, stream, &o, &vf);
+}
+
+int topk_block_max(const float* logits, int64_t row_stride, int32_t num_rows, float* bmax,
+                   int64_t bmax_stride, hipStream_t stream) {
+  if (num_rows < 0 || row_stride < 1 || row_stride >= ((int64_t)1 << 30)) return TOPK_EINVAL;
+  if (num_rows == 0) return TOPK_OK;
+  if (!logits || !bmax) return TOPK_EINVAL;
+  const int64_t nb = (row_stride + 31) / 32;
+  if (bmax_stride < nb) return TOPK_EINVAL;
+  if (!aligned(logits, 4) || !aligned(bmax, 4)) return TOPK_ELAYOUT;
+  const int64_t total = (int64_t)num_rows * nb;
+  const int64_t grid = (total + 255) / 256;
+  if (grid >= ((int64_t)1 << 31)) return TOPK_EINVAL;
+  int32_t nr = num_rows;
+  void* args[] = {const_cast<float**>(&logits), &row_stride, &nr, &bmax, &bmax_stride};
+  if (hipLaunchKernel(block_max_kernel_ptr(), dim3((unsigned)grid), dim3(256), args, 0, stream) !=
+      hipSuccess)
+    return TOPK_ELAUNCH;
+  if (hipGetLastError() != hipSuccess) return TOPK_ELAUNCH;
+  return TOPK_OK;
+}
+
+int topk_decode_blockskip(const float* logits, int64_t row_stride, const int32_t* n_valid,
+                          const float* bmax, int64_t bmax_stride, int32_t num_rows, int32_t k,
+                          int32_t* indices, float* values, uint32_t flags, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  topk_options o;
+  memset(&o, 0, sizeof(o));
+  o.values = values;
+  o.flags = flags;
+  o.bmax = bmax;
+  o.bmax_stride = bmax_stride;
+  if (!bmax && num_rows > 0) return TOPK_EINVAL;
+  return run(0, logits, row_stride, n_valid, nullptr, num_rows, k, indices, 0, workspace,
+             workspace_bytes, stream, &o);
 }
 
 int topk_decode_varlen_ex(const float* logits, int64_t row_stride, const int32_t* kv_lens,

@@ -169,6 +169,30 @@ int topk_decode_varlen_hinted(const float* logits, int64_t row_stride, const int
                               float* values, uint32_t flags, void* workspace,
                               size_t workspace_bytes, hipStream_t stream);
 
+/* ---- Block-skip pass --------------------------------------------------------
+ * Decode form with per-32-score block maxima (PR 18122 "Description" and its
+ * block-skip commit): the pass reads bmax and visits only the score blocks
+ * whose maximum can reach the sampled threshold, then selects exactly as the
+ * other forms do (same result, same output options).
+ *  bmax: device float [num_rows][bmax_stride], bmax_stride >= ceil(row_stride
+ *      / 32) (else TOPK_EINVAL), 4-byte aligned.  bmax[r][i] must be at least
+ *      every score of logits[r, 32i : 32i + 32) inside the row's window (an
+ *      upper bound suffices: NaN or +inf make a block always visited); with a
+ *      smaller value the result is unspecified.  topk_block_max writes the
+ *      exact maxima (the indexer GEMM's epilogue would in production).
+ *  Gate (shape only): num_rows * row_stride * 4 >= 128 MiB and row_stride >=
+ *  72 * k; other calls take the ordinary decode path, bmax unused.  The pass
+ *  uses no workspace; hints are not used by it. */
+int topk_decode_blockskip(const float* logits, int64_t row_stride, const int32_t* n_valid,
+                          const float* bmax, int64_t bmax_stride, int32_t num_rows, int32_t k,
+                          int32_t* indices, float* values, uint32_t flags, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
+/* bmax[r][i] = max over logits[r, 32i : min(32i + 32, row_stride)) (NaN
+ * ignored unless the whole block is NaN), for i < ceil(row_stride / 32). */
+int topk_block_max(const float* logits, int64_t row_stride, int32_t num_rows, float* bmax,
+                   int64_t bmax_stride, hipStream_t stream);
+
 /* Bytes of workspace a call with num_rows rows of stride `max_row_len` needs
  * (pass the row_stride of the call; 0 when the plan uses one workgroup per
  * row and needs none).  The value does not depend on the device.  Returns 0
@@ -199,7 +223,11 @@ const char* topk_strerror(int status);
  *          lowest hint score when hints steered it), [5] of its high end,
  *      [6] workgroups per row, [7] candidate cap,
  *      [8] split rows: the floor bin the row's histogram counts from (-1 for
- *          one-workgroup rows and rows without a valid bracket).
+ *          one-workgroup rows and rows without a valid bracket); block-skip
+ *          rows: the score blocks the last walk visited.
+ *  Block-skip rows report path 1 (survivors only), 5 (counts short of k: every
+ *  block recounted without a floor), 3 (crossing bin over the member cap) or 2
+ *  (invalid bracket or forced rescue: radix select over the whole row).
  */
 #define TOPK_STATS_WORDS 9
 
@@ -212,6 +240,10 @@ typedef struct topk_options {
   const int32_t* pre_idx; /* as in topk_decode_hinted (decode forms only,
                              else TOPK_EINVAL) */
   int64_t pre_idx_stride;
+  const float* bmax;      /* as in topk_decode_blockskip (decode forms only) */
+  int64_t bmax_stride;
+  int32_t blockskip;      /* with bmax: 0 = the gate decides, 1 = always the
+                             block-skip pass, -1 = never */
 } topk_options;
 
 int topk_decode_ex(const float* logits, int64_t row_stride, const int32_t* n_valid,

@@ -169,6 +169,26 @@ def test_output_options_and_varlen_validation():
     o = ert._Options(0, 0, None, None, 0, P16, 512)
     assert lib.topk_prefill_ex(P16, 4096, P16, P16, 4, 512, P16, 0, None, 0, None,
                                ctypes.pointer(o)) == ert.TOPK_EINVAL
+    # block-skip: bmax stride below ceil(row_stride / 32), a forced pass
+    # without maxima, maxima on the prefill form, a misaligned bmax
+    assert lib.topk_decode_blockskip(P16, 4096, P16, P16, 127, 4, 512, P16, None, 0, None, 0,
+                                     None) == ert.TOPK_EINVAL
+    assert lib.topk_decode_blockskip(P16, 4096, P16, None, 128, 4, 512, P16, None, 0, None, 0,
+                                     None) == ert.TOPK_EINVAL
+    assert lib.topk_decode_blockskip(P16, 4096, P16, P16 + 2, 128, 4, 512, P16, None, 0, None, 0,
+                                     None) == ert.TOPK_ELAYOUT
+    o = ert._Options(0, 0, None, None, 0, None, 0, P16, 128, 0)
+    assert lib.topk_prefill_ex(P16, 4096, P16, P16, 4, 512, P16, 0, None, 0, None,
+                               ctypes.pointer(o)) == ert.TOPK_EINVAL
+    o = ert._Options(0, 0, None, None, 0, None, 0, None, 0, 1)
+    assert lib.topk_decode_ex(P16, 4096, P16, 4, 512, P16, None, 0, None,
+                              ctypes.pointer(o)) == ert.TOPK_EINVAL
+    o = ert._Options(0, 0, None, None, 0, None, 0, P16, 128, 2)
+    assert lib.topk_decode_ex(P16, 4096, P16, 4, 512, P16, None, 0, None,
+                              ctypes.pointer(o)) == ert.TOPK_EINVAL
+    assert lib.topk_block_max(P16, 4096, 4, P16, 127, None) == ert.TOPK_EINVAL
+    assert lib.topk_block_max(P16, 0, 4, P16, 128, None) == ert.TOPK_EINVAL
+    assert lib.topk_block_max(None, 4096, 0, None, 0, None) == 0
     # empty batches are a no-op for every form
     assert lib.topk_decode_varlen(None, 4096, None, 0, 2, 4, 512, None, None, 0, None, 0,
                                   None) == 0

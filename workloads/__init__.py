@@ -195,6 +195,40 @@ def decode_step(rows: int = 64, stride: int = 131072, k: int = 2048, lo: int = 8
 
 
 # --------------------------------------------------------------------------
+# Block-skip batch: at the block-skip gate's size, rows with locality.
+# --------------------------------------------------------------------------
+def decode_blockskip(rows: int = 256, stride: int = 131072, k: int = 512, lo: int = 65536,
+                     hi: int = 131072, cfg: int = 7, smooth: float = 2.0,
+                     span: int = 256) -> Workload:
+    """A decode batch at the block-skip gate's size: rows * stride * 4 =
+    128 MiB and stride >= 72 K (PR 18122 "Description").  Scores are N(0, 1)
+    noise plus a smooth component -- N(0, smooth^2) knots every `span`
+    positions, linearly interpolated -- so high scores gather in stretches
+    of the row, as attention scores do around the tokens a query attends to
+    (the pages measure captured decode rows, which are not public; this
+    locality stands in for theirs).  smooth = 0 gives i.i.d. rows, the
+    case where block maxima skip least.  n_valid uniform in [lo, hi]; the pad
+    is poisoned (+inf, NaN, 3e38)."""
+    x = np.empty((rows, stride), dtype=np.float32)
+    nv = np.empty(rows, dtype=np.int32)
+    knots = stride // span + 2
+    grid = np.arange(stride, dtype=np.float64) / span
+    for r in range(rows):
+        g = row_rng(cfg, r)
+        n_r = int(g.integers(lo, hi, endpoint=True))
+        nv[r] = n_r
+        row = g.standard_normal(stride)
+        if smooth > 0.0:
+            kv = smooth * g.standard_normal(knots)
+            row += np.interp(grid, np.arange(knots, dtype=np.float64), kv)
+        row = row.astype(np.float32)
+        _poison_row_outside(row, 0, n_r, POISON_DECODE)
+        x[r] = row
+    tag = "bsk" if smooth > 0.0 else "bsk_iid"
+    return Workload(f"decode_{tag}_{rows}x{stride}_k{k}", "decode", x, k, n_valid=nv)
+
+
+# --------------------------------------------------------------------------
 # Workload 3: prefill packed causal tile, 4 x 1024 rows, stride 16640, K=1024.
 # --------------------------------------------------------------------------
 PREFILL_OFFSETS = (0, 65, 130, 195)
