@@ -43,11 +43,13 @@ namespace ert {
 namespace {
 
 constexpr int kBskBlock = 1024;   // threads per row
-constexpr int kBskCap = 8192;     // survivor list capacity (blocks)
+constexpr int kBskCap = kBskMaxBlocks;  // survivor list / maxima capacity (blocks)
 constexpr int kBskMembers = 2048; // crossing-bin members kept in LDS
 
+template <bool SELF>
 struct alignas(16) BskSmem {
   uint32_t hist[kBins + 64];  // + one trash word per lane
+  float bm[SELF ? kBskCap : 1];  // block maxima made by the first pass
   uint32_t list[kBskCap];     // survivor block ids
   uint32_t key[kBskMembers];
   int32_t idx[kBskMembers];
@@ -62,13 +64,13 @@ struct alignas(16) BskSmem {
 
 }  // namespace
 
-template <int K>
+template <int K, bool SELF>
 __global__ void __launch_bounds__(kBskBlock) topk_blockskip_kernel(const GvrParams p,
                                                                    const float* bmax,
                                                                    int64_t bmax_stride) {
   constexpr int BLOCK = kBskBlock;
   constexpr int W = BLOCK / 64;
-  __shared__ BskSmem sm;
+  __shared__ BskSmem<SELF> sm;
 
   const int t = threadIdx.x;
   const int l = lane_id();
@@ -88,9 +90,41 @@ __global__ void __launch_bounds__(kBskBlock) topk_blockskip_kernel(const GvrPara
     return;
   }
   const float* win = p.logits + row * (int64_t)S + ks;
-  const float* bm_row = bmax + row * bmax_stride;
+  const float* bm_row = SELF ? sm.bm : bmax + row * bmax_stride;
   const int nb = (nv + 31) >> 5;  // blocks of the window
   const float qnan = __builtin_nanf("");
+
+  const f4* win4 = reinterpret_cast<const f4*>(win);
+  if (SELF) {
+    // ---- first pass: every block once, its maximum kept in LDS -----------
+    // (streaming rows of up to kBskCap blocks; U loads in flight per lane)
+    constexpr int U = 8;
+    const int sub = l & 7;
+    for (int s0 = w * 8; s0 < nb; s0 += W * 8 * U) {
+      f4 x[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int sb = s0 + u * W * 8 + (l >> 3);
+        const int q = sb * 32 + sub * 4;
+        x[u] = f4{-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
+        if (sb < nb && q < nv) x[u] = __builtin_nontemporal_load(win4 + (q >> 2));
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int sb = s0 + u * W * 8 + (l >> 3);
+        const int q = sb * 32 + sub * 4;
+        float m = -__builtin_inff();
+#pragma unroll
+        for (int e = 0; e < 4; ++e) m = (q + e < nv) ? fmaxf(m, x[u][e]) : m;
+        // maximum over the block's 8 lanes
+        m = fmaxf(m, __shfl_xor(m, 1, 64));
+        m = fmaxf(m, __shfl_xor(m, 2, 64));
+        m = fmaxf(m, __shfl_xor(m, 4, 64));
+        if (sub == 0 && sb < nb) sm.bm[sb] = m;
+      }
+    }
+    __syncthreads();
+  }
 
   // ---- guess from the block maxima ----------------------------------------
   // The K largest block maxima are K distinct scores of the row, so the K-th
@@ -222,7 +256,6 @@ __global__ void __launch_bounds__(kBskBlock) topk_blockskip_kernel(const GvrPara
   // Decode windows start at the row's 16-byte aligned base and the stride is
   // a multiple of 4, so a group that starts inside the window lies inside the
   // row; lanes past the window's end take no score.
-  const f4* win4 = reinterpret_cast<const f4*>(win);
   auto walk = [&](auto&& f) {
     constexpr int U = 4;  // steps whose loads are in flight together
     const int nwalk = nlist < 0 ? nb : nlist;
@@ -409,11 +442,17 @@ __global__ void __launch_bounds__(256) block_max_kernel(const float* logits, int
   bmax[r * bmax_stride + i] = m;
 }
 
-const void* blockskip_kernel(int k) {
+const void* blockskip_kernel(int k, bool self) {
   switch (k) {
-    case 512: return reinterpret_cast<const void*>(&topk_blockskip_kernel<512>);
-    case 1024: return reinterpret_cast<const void*>(&topk_blockskip_kernel<1024>);
-    case 2048: return reinterpret_cast<const void*>(&topk_blockskip_kernel<2048>);
+    case 512:
+      return self ? reinterpret_cast<const void*>(&topk_blockskip_kernel<512, true>)
+                  : reinterpret_cast<const void*>(&topk_blockskip_kernel<512, false>);
+    case 1024:
+      return self ? reinterpret_cast<const void*>(&topk_blockskip_kernel<1024, true>)
+                  : reinterpret_cast<const void*>(&topk_blockskip_kernel<1024, false>);
+    case 2048:
+      return self ? reinterpret_cast<const void*>(&topk_blockskip_kernel<2048, true>)
+                  : reinterpret_cast<const void*>(&topk_blockskip_kernel<2048, false>);
     default: return nullptr;
   }
 }

@@ -39,6 +39,7 @@ constexpr int kSplitQpt[] = {4, 8, 17};
 constexpr int kMaxWgsPerRow = 64;
 constexpr int kMaxSlots = 256;  // split rows per launch (workspace slots)
 constexpr int kStatsWords = 9;
+constexpr int kBskMaxBlocks = 8192;  // rows the streaming pass takes: <= this many blocks of 32
 
 // Workspace layout (bytes):
 //   [0, 256)                             error flags (word 0)

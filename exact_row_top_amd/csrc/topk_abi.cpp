@@ -14,7 +14,7 @@
 namespace ert {
 const void* gvr_kernel(int k, int block, int qpt, bool split);
 const void* epilogue_kernel(int k);
-const void* blockskip_kernel(int k);
+const void* blockskip_kernel(int k, bool self);
 const void* block_max_kernel_ptr();
 }
 
@@ -275,7 +275,8 @@ int run(int mode, const float* logits, int64_t row_stride, const int32_t* e1, co
   }
   const float* bmax = opts ? opts->bmax : nullptr;
   const int32_t bsk_mode = opts ? opts->blockskip : 0;
-  if (bsk_mode < -1 || bsk_mode > 1) return TOPK_EINVAL;
+  if (bsk_mode < -1 || bsk_mode > 2) return TOPK_EINVAL;
+  if (bsk_mode == 2 && (mode != 0 || (row_stride + 31) / 32 > kBskMaxBlocks)) return TOPK_EINVAL;
   if (bmax) {
     if (mode != 0) return TOPK_EINVAL;  // block-skip serves the decode forms
     if (opts->bmax_stride < (row_stride + 31) / 32) return TOPK_EINVAL;
@@ -308,9 +309,11 @@ int run(int mode, const float* logits, int64_t row_stride, const int32_t* e1, co
   prm.indices = indices;
   prm.row_stats = opts ? opts->row_stats : nullptr;
 
-  if (bmax && bsk_mode >= 0 && (bsk_mode == 1 || blockskip_gate(num_rows, row_stride, k))) {
-    // block-skip pass: one 1024-thread workgroup per row, no workspace
-    const void* kern = blockskip_kernel(k);
+  if (bsk_mode == 2 || (bmax && bsk_mode >= 0 &&
+                        (bsk_mode == 1 || blockskip_gate(num_rows, row_stride, k)))) {
+    // block-skip pass: one 1024-thread workgroup per row, no workspace; mode
+    // 2 streams every block once and makes the maxima itself
+    const void* kern = blockskip_kernel(k, bsk_mode == 2);
     if (!kern) return TOPK_EINVAL;
     prm.wgs_per_row = 1;
     prm.rows = num_rows;

@@ -243,7 +243,10 @@ typedef struct topk_options {
   const float* bmax;      /* as in topk_decode_blockskip (decode forms only) */
   int64_t bmax_stride;
   int32_t blockskip;      /* with bmax: 0 = the gate decides, 1 = always the
-                             block-skip pass, -1 = never */
+                             block-skip pass, -1 = never; 2 = the pass with
+                             maxima it makes itself in a first streaming pass
+                             (decode forms, rows of at most 8192 blocks of
+                             32; bmax unused) */
 } topk_options;
 
 int topk_decode_ex(const float* logits, int64_t row_stride, const int32_t* n_valid,

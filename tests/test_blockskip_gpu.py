@@ -206,3 +206,28 @@ def test_blockskip_gate(ert):
             assert all(s[r, 6] == 1 and s[r, 8] > 0 for r in range(w.num_rows)), s
         else:
             assert all(s[r, 6] > 1 for r in range(w.num_rows)), s
+
+
+@pytest.mark.parametrize("k", [512, 2048])
+def test_streaming_pass_with_its_own_maxima(ert, k):
+    """blockskip=2: the pass streams every block once, keeps its maxima in LDS
+    and continues as with given maxima (no producer needed)."""
+    import torch
+    w = workloads.decode_blockskip(rows=10, stride=max(65536, 80 * k), k=k, lo=k // 2,
+                                   hi=max(65536, 80 * k), cfg=90 + k)
+    g = np.random.default_rng(k)
+    w.logits[1, : int(w.n_valid[1])] = np.floor(4.0 * g.random(int(w.n_valid[1]))) - 1.5
+    w.logits[2, : int(w.n_valid[2])] = np.float32(0.5)
+    want = oracle.topk_workload(w)
+    dev = to_dev(w)
+    for kw in ({}, {"deterministic": True, "sorted": True}):
+        log(f"[stream] k={k} {kw}")
+        st = torch.full((w.num_rows, ert.STATS_WORDS), -7, dtype=torch.int32, device="cuda")
+        got = ert.topk_decode(dev["logits"], dev["n_valid"], k, blockskip=2, row_stats=st, **kw)
+        torch.cuda.synchronize()
+        got = got.cpu().numpy()
+        assert_parity(w, got, want)
+        if kw:
+            assert np.array_equal(got, want)
+        s = st.cpu().numpy()
+        assert all(s[r, 6] == 1 for r in range(w.num_rows)), s
