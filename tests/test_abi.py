@@ -183,8 +183,15 @@ def test_output_options_and_varlen_validation():
     o = ert._Options(0, 0, None, None, 0, None, 0, None, 0, 1)
     assert lib.topk_decode_ex(P16, 4096, P16, 4, 512, P16, None, 0, None,
                               ctypes.pointer(o)) == ert.TOPK_EINVAL
-    o = ert._Options(0, 0, None, None, 0, None, 0, P16, 128, 2)
+    o = ert._Options(0, 0, None, None, 0, None, 0, P16, 128, 3)
     assert lib.topk_decode_ex(P16, 4096, P16, 4, 512, P16, None, 0, None,
+                              ctypes.pointer(o)) == ert.TOPK_EINVAL
+    # the streaming pass (blockskip=2): decode forms only, rows of at most
+    # 8192 blocks of 32
+    o = ert._Options(0, 0, None, None, 0, None, 0, None, 0, 2)
+    assert lib.topk_prefill_ex(P16, 4096, P16, P16, 4, 512, P16, 0, None, 0, None,
+                               ctypes.pointer(o)) == ert.TOPK_EINVAL
+    assert lib.topk_decode_ex(P16, 8192 * 32 + 4, P16, 4, 512, P16, None, 0, None,
                               ctypes.pointer(o)) == ert.TOPK_EINVAL
     assert lib.topk_block_max(P16, 4096, 4, P16, 127, None) == ert.TOPK_EINVAL
     assert lib.topk_block_max(P16, 0, 4, P16, 128, None) == ert.TOPK_EINVAL
