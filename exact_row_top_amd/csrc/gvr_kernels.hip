@@ -583,11 +583,23 @@ __global__ void __launch_bounds__(BLOCK)
       floor_bin = blo;
       // A sample bin at or above the floor holding 8 or more samples marks a
       // row with heavy ties there: its histogram pass aggregates per wave.
+      // One holding so many that its scores (each sample stands for nv / K
+      // of them) would fill the member list twice over predicts a crossing
+      // bin over the cap: such a bin cannot lie above the crossing (it holds
+      // more than K scores) nor between the floor and it (the floor's count
+      // would pass lam + margin there), so the row goes straight to the
+      // rescue instead of paying for the fast path first.
+      const float crowded = 2.0f * (float)kSingleCap * (float)K / (float)nv;
       for (int i = t; i < kBins + 64; i += BLOCK) {
-        if (i < kBins && i >= blo && sm.u.hist[i] >= 8u) sm.bc[3] = 1u;
+        if (i < kBins && i >= blo) {
+          const uint32_t c = sm.u.hist[i];
+          if (c >= 8u) sm.bc[3] = 1u;
+          if ((float)c >= crowded) sm.ctr[3] = 1u;
+        }
         sm.u.hist[i] = 0u;
       }
-      path = 1;
+      __syncthreads();
+      path = sm.ctr[3] ? 3 : 1;
     }
     if (path == 1) {
       // ---- verify (a4): the row's histogram on bins >= blo ----------------
