@@ -223,6 +223,21 @@ bool blockskip_gate(int32_t num_rows, int64_t row_stride, int32_t k) {
   return (int64_t)num_rows * row_stride * 4 >= ((int64_t)128 << 20) && row_stride >= (int64_t)72 * k;
 }
 
+// Streaming tier (the block-skip pass making its own maxima) for batches of
+// many long decode rows: at least 128 rows, rows longer than one resident
+// workgroup holds and at least 4 K whole blocks of 32 per row (so the K-th
+// largest block maximum gives the floor), up to the pass's 8192 blocks.
+// Measured on MI355X against the resident tiers (i.i.d. rows; rows with
+// locality gain 2-4x more): 128 x 131072 K=512 32.8 vs 35.5 us, 1024 x 65536
+// K=512 101 vs 123 us, 512 x 131072 K=512 71 vs 136 us, 256 x 262144 K=2048
+// 86 vs 135 us; shapes it loses on (256 x 65536 K=1024, 512 x 65536 K=2048,
+// 256 x 131072 K=2048) fail the 4 K blocks rule.
+bool stream_gate(int32_t num_rows, int64_t row_stride, int32_t k) {
+  const int64_t single_max = (int64_t)kSingleVariants[3].block * kSingleVariants[3].qpt * 4;
+  return num_rows >= 128 && row_stride > single_max && row_stride / 32 >= (int64_t)4 * k &&
+         (row_stride + 31) / 32 <= kBskMaxBlocks;
+}
+
 // Output stage after the selection: values and / or sorted long rows.
 int launch_epilogue(const GvrParams& prm, int32_t k, int32_t num_rows, float* values,
                     uint32_t flags, hipStream_t stream) {
@@ -309,16 +324,20 @@ int run(int mode, const float* logits, int64_t row_stride, const int32_t* e1, co
   prm.indices = indices;
   prm.row_stats = opts ? opts->row_stats : nullptr;
 
-  if (bsk_mode == 2 || (bmax && bsk_mode >= 0 &&
-                        (bsk_mode == 1 || blockskip_gate(num_rows, row_stride, k)))) {
-    // block-skip pass: one 1024-thread workgroup per row, no workspace; mode
-    // 2 streams every block once and makes the maxima itself
-    const void* kern = blockskip_kernel(k, bsk_mode == 2);
+  const bool given = bmax && bsk_mode >= 0 &&
+                     (bsk_mode == 1 || blockskip_gate(num_rows, row_stride, k));
+  const bool self = !given && (bsk_mode == 2 || (mode == 0 && bsk_mode == 0 && force_g == 0 &&
+                                                 !(opts && opts->force_rescue) &&
+                                                 stream_gate(num_rows, row_stride, k)));
+  if (given || self) {
+    // block-skip pass: one 1024-thread workgroup per row, no workspace; the
+    // streaming form reads every block once and makes the maxima itself
+    const void* kern = blockskip_kernel(k, self);
     if (!kern) return TOPK_EINVAL;
     prm.wgs_per_row = 1;
     prm.rows = num_rows;
     prm.row_begin = 0;
-    int64_t bstride = opts->bmax_stride;
+    int64_t bstride = given ? opts->bmax_stride : 0;  // opts may be null here
     void* args[] = {&prm, &bmax, &bstride};
     if (hipLaunchKernel(kern, dim3((unsigned)num_rows), dim3(1024), args, 0, stream) != hipSuccess)
       return TOPK_ELAUNCH;

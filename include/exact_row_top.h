@@ -182,7 +182,11 @@ int topk_decode_varlen_hinted(const float* logits, int64_t row_stride, const int
  *      exact maxima (the indexer GEMM's epilogue would in production).
  *  Gate (shape only): num_rows * row_stride * 4 >= 128 MiB and row_stride >=
  *  72 * k; other calls take the ordinary decode path, bmax unused.  The pass
- *  uses no workspace; hints are not used by it. */
+ *  uses no workspace; hints are not used by it.
+ *  Without bmax, decode calls of at least 128 rows whose row_stride exceeds
+ *  what one resident workgroup holds (36864) and spans at least 4 * k blocks
+ *  of 32 (up to 8192) take the pass in its streaming form, which makes the
+ *  maxima itself (topk_options.blockskip = -1 keeps the resident tiers). */
 int topk_decode_blockskip(const float* logits, int64_t row_stride, const int32_t* n_valid,
                           const float* bmax, int64_t bmax_stride, int32_t num_rows, int32_t k,
                           int32_t* indices, float* values, uint32_t flags, void* workspace,

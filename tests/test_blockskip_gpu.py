@@ -231,3 +231,31 @@ def test_streaming_pass_with_its_own_maxima(ert, k):
             assert np.array_equal(got, want)
         s = st.cpu().numpy()
         assert all(s[r, 6] == 1 for r in range(w.num_rows)), s
+
+
+def test_many_long_rows_take_the_streaming_tier(ert):
+    """128+ decode rows longer than one resident workgroup holds, with at
+    least 4 K blocks per row: the plan streams them (one workgroup per row,
+    maxima made in the kernel) -- exact, rows with locality included."""
+    import torch
+    k = 512
+    w = workloads.decode_blockskip(rows=128, stride=65536, k=k, lo=700, hi=65536, cfg=95)
+    want = oracle.topk_workload(w)
+    dev = to_dev(w)
+    # the plain entry point (no options at all) plans the streaming tier too
+    got = ert.topk_decode(dev["logits"], dev["n_valid"], k)
+    torch.cuda.synchronize()
+    assert_parity(w, got.cpu().numpy(), want)
+    st = torch.full((w.num_rows, ert.STATS_WORDS), -7, dtype=torch.int32, device="cuda")
+    got = ert.topk_decode(dev["logits"], dev["n_valid"], k, row_stats=st)
+    torch.cuda.synchronize()
+    assert_parity(w, got.cpu().numpy(), want)
+    s = st.cpu().numpy()
+    long_rows = [r for r in range(w.num_rows) if int(w.n_valid[r]) > k]
+    assert all(s[r, 6] == 1 and s[r, 8] > 0 for r in long_rows), s[:4]
+    # blockskip=-1 keeps the resident tiers
+    st2 = torch.full((w.num_rows, ert.STATS_WORDS), -7, dtype=torch.int32, device="cuda")
+    got = ert.topk_decode(dev["logits"], dev["n_valid"], k, row_stats=st2, blockskip=-1)
+    torch.cuda.synchronize()
+    assert_parity(w, got.cpu().numpy(), want)
+    assert all(st2.cpu().numpy()[r, 6] > 1 for r in long_rows)
