@@ -588,8 +588,11 @@ __global__ void __launch_bounds__(BLOCK)
       // bin over the cap: such a bin cannot lie above the crossing (it holds
       // more than K scores) nor between the floor and it (the floor's count
       // would pass lam + margin there), so the row goes straight to the
-      // rescue instead of paying for the fast path first.
-      const float crowded = 2.0f * (float)kSingleCap * (float)K / (float)nv;
+      // rescue instead of paying for the fast path first.  At least 32
+      // samples, half a sample block: a few neighbouring scores of one block
+      // can share a bin on a smooth stretch of the row without the row being
+      // crowded.
+      const float crowded = fmaxf(2.0f * (float)kSingleCap * (float)K / (float)nv, 32.0f);
       for (int i = t; i < kBins + 64; i += BLOCK) {
         if (i < kBins && i >= blo) {
           const uint32_t c = sm.u.hist[i];
