@@ -56,7 +56,7 @@ struct SlotHeader {
   uint32_t bar_count;  // barrier arrivals of the current row
   uint32_t done;       // workgroups finished with the slot (last one cleans)
   uint32_t win_cur;    // winner output cursor (rescue)
-  uint32_t cand_cur;   // spare cursor
+  uint32_t cand_cur;   // the row's maximum as an order-preserving key (retry)
   uint32_t tie_cur;    // tie tickets (rescue)
   uint32_t pad[59];    // header is 256 bytes
 };

@@ -201,8 +201,8 @@ __global__ void __launch_bounds__(BLOCK)
   // those of the whole hint set.  The split tier reads them up front: its
   // positions first, so that the scores are gathered before the part's loads
   // are issued and the bracket overlaps the part's flight as it does without
-  // hints.  A one-workgroup row reads them only when its first bracket fails
-  // (below): there a retry costs one histogram pass in LDS.
+  // hints.  A one-workgroup row does not read them: when its first bracket
+  // fails it retries with the row's own maximum, which it holds (below).
   const int32_t* hrow = nullptr;
   if (p.hints) {
     // rows and hint_div are positive int32: a 32-bit unsigned divide
@@ -394,72 +394,99 @@ __global__ void __launch_bounds__(BLOCK)
   int path = 2;  // 1 fast, 2 rescue (invalid bracket), 3 rescue (crowded top)
   Cross cr{-1, 0u, 0u, 0u};
 
+  float xf = -__builtin_inff();  // one-workgroup retry: the counted scores' floor
   if (!SPLIT) {
     // ==== one workgroup per row ============================================
     if (bracket_ok) {
       // ---- verify (a4, a5): LDS histogram and crossing bin ---------------
-      auto verify = [&]() {
-        each([&](int j, int q, bool full) {
-          if (full) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) lds_inc(hword(sm.u.hist, vbin_off(v[j][e], bm)));
-          } else {
+      // (masked: only scores >= xf are counted -- the retry below)
+      auto verify = [&](const bool masked) {
+        if (masked) {
+          each([&](int j, int q, bool) {
+            int b[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const float x = v[j][e];
-              lds_inc(hword(sm.u.hist, (x == x) ? vbin_off(x, bm) : 4u * (uint32_t)(kBins + l)));
+              b[e] = x >= xf ? (int)vbin_off(x, bm) : -1;
             }
-          }
-        });
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (b[e] >= 0) lds_inc(hword(sm.u.hist, (uint32_t)b[e]));
+          });
+        } else {
+          each([&](int j, int q, bool full) {
+            if (full) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) lds_inc(hword(sm.u.hist, vbin_off(v[j][e], bm)));
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float x = v[j][e];
+                lds_inc(hword(sm.u.hist, (x == x) ? vbin_off(x, bm) : 4u * (uint32_t)(kBins + l)));
+              }
+            }
+          });
+        }
         __syncthreads();
         find_crossing<kBins, BLOCK>([&](int b) { return sm.u.hist[b]; }, (uint32_t)K, &sm.cross,
                                     sm.scan);
         cr = read_cross(&sm.cross);
         path = (cr.b >= 0 && cr.m <= (uint32_t)kSingleCap) ? 1 : 3;
       };
-      verify();
-      if (path == 3 && hrow) {
-        // Hint-guided retry: the crossing bin is over the cap.  When the
-        // hints reach above the sample's maximum (peaks the sample missed,
-        // piled into the top bin), raise the bracket's top to them and
-        // count again; otherwise the rescue below finishes the row.
-        float x = qnan;
-        if (t < K) {
-          const int32_t hp = hrow[t];
-          if ((uint32_t)hp < (uint32_t)nv) x = rowp[ks + hp];
-        }
-        float hlo = x, hhi = x;
-        wave_minmax(hlo, hhi);
-        if (l == 0) {
-          sm.hmin[w] = hlo;
-          sm.hmax[w] = hhi;
+      verify(false);
+      if (path == 3 && cr.b == kBins - 1) {
+        // The crossing bin is the top one, over the cap: scores above the
+        // sample's maximum (peaks the sample missed) pile up there.  Count
+        // again over [that bin's lower edge, the row's own maximum], only
+        // the scores at or above the edge (a crowd at the maximum itself
+        // still takes the rescue).
+        float mx = -__builtin_inff();
+        each([&](int j, int q, bool) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) mx = fmaxf(mx, v[j][e]);  // NaN markers drop out
+        });
+        float mn = mx;
+        wave_minmax(mn, mx);
+        if (l == 0) sm.hmax[w] = mx;
+        if (w == 0) {
+          const float e = bin_edge(kBins - 1, bm);
+          if (l == 0) sm.thr[0] = e;
         }
         __syncthreads();
-        float hl, hh;
-        hint_extremes(hl, hh);
-        if (__builtin_isfinite(hl) && __builtin_isfinite(hh) && hh > hl && hh > gmax) {
-          const float sc = (float)kBins / (hh - gmin);
-          const float c0 = -gmin * sc;
-          if (__builtin_isfinite(hh - gmin) && __builtin_isfinite(4.0f * sc) &&
-              __builtin_isfinite(4.0f * c0) && sc > 0.0f) {
-            gmax = hh;
-            bm.sc = sc;
-            bm.c0 = c0;
-            bm.sc4 = 4.0f * sc;
-            bm.c04 = 4.0f * c0;
-            for (int i = t; i < kBins + 64; i += BLOCK) sm.u.hist[i] = 0u;
-            __syncthreads();
-            verify();
-          }
+        float top = sm.hmax[0];
+#pragma unroll
+        for (int i = 1; i < W; ++i) top = fmaxf(top, sm.hmax[i]);
+        top = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(top)));
+        const float lo = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sm.thr[0])));
+        const float sc = (float)kBins / (top - lo);
+        const float c0 = -lo * sc;
+        if (__builtin_isfinite(lo) && __builtin_isfinite(top) && top > lo &&
+            __builtin_isfinite(top - lo) && __builtin_isfinite(4.0f * sc) &&
+            __builtin_isfinite(4.0f * c0) && sc > 0.0f) {
+          gmin = lo;
+          gmax = top;
+          bm.gmin = lo;
+          bm.sc = sc;
+          bm.c0 = c0;
+          bm.sc4 = 4.0f * sc;
+          bm.c04 = 4.0f * c0;
+          xf = lo;
+          for (int i = t; i < kBins + 64; i += BLOCK) sm.u.hist[i] = 0u;
+          __syncthreads();
+          verify(true);
+          if (path == 1) path = 5;
         }
       }
     }
-    if (path == 1) {
+    if (path == 1 || path == 5) {
       // ---- compaction (a6) ------------------------------------------------
       // bin > b*  <=>  x >= x_hi (winner);  bin == b*  <=>  x_lo <= x < x_hi
+      // (after the retry bin 0 also holds what lies below its floor xf)
       if (w < 2) {
+        // (the upper edge of the top bin is NaN, which no score reaches: no
+        // clamp there)
         const float e = bin_edge(cr.b + w, bm);
-        if (l == 0) sm.thr[w] = e;
+        if (l == 0) sm.thr[w] = w == 0 ? fmaxf(e, xf) : e;
       }
       __syncthreads();
       const uint32_t need = (uint32_t)K - cr.above;
@@ -536,7 +563,7 @@ __global__ void __launch_bounds__(BLOCK)
         list_select<BLOCK>(sm.u.c.key, sm.u.c.idx, m, need, p.deterministic != 0, out, cr.above,
                            (uint32_t)K, sm.dh, &sm.cross, sm.scan, sm.ctr, nbar);
       }
-      put_stats(1, (int)cr.m, (int)cr.above, cr.b);
+      put_stats(path, (int)cr.m, (int)cr.above, cr.b);
       return;
     }
   } else {
@@ -604,7 +631,13 @@ __global__ void __launch_bounds__(BLOCK)
       __syncthreads();
       path = sm.ctr[3] ? 3 : 1;
     }
-    if (path == 1) {
+    // One verify round: the part's scores >= edge(bl) counted per bin in
+    // LDS, merged into gh (zero on entry) through the workspace behind a row
+    // barrier, the crossing bin -> cr.  Returns the path: 1 fast, 3 crowded
+    // crossing bin, 4 merged counts short of K (the floor lay above the K-th
+    // value).
+    float xfloor = -__builtin_inff();  // a retry's explicit floor value
+    auto verify = [&](const int bl, uint32_t* gh) -> int {
       // ---- verify (a4): the row's histogram on bins >= blo ----------------
       // Each workgroup counts its part's scores >= edge(blo) per bin in LDS,
       // adds the non-zero counts into the row's histogram in the workspace
@@ -615,11 +648,11 @@ __global__ void __launch_bounds__(BLOCK)
       // below blo are not needed: were the crossing bin there, the merged
       // counts would not reach K and the row would take the rescue.
       if (w == 0) {
-        const float e = bin_edge(blo, bm);
+        const float e = bin_edge(bl, bm);
         if (l == 0) sm.thr[0] = e;
       }
       __syncthreads();
-      const float xf = sm.thr[0];
+      const float xf = fmaxf(sm.thr[0], xfloor);
       if (sm.bc[3]) {
         each([&](int j, int q, bool) {
 #pragma unroll
@@ -645,7 +678,6 @@ __global__ void __launch_bounds__(BLOCK)
         });
       }
       __syncthreads();
-      uint32_t* gh = sf->hist;
       {
         constexpr int PER = kBins / BLOCK;
         const int hi = kBins - 1 - t * PER;
@@ -653,7 +685,7 @@ __global__ void __launch_bounds__(BLOCK)
         uint32_t sum = 0;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-          c[i] = hi - i >= blo ? sm.u.hist[hi - i] : 0u;
+          c[i] = hi - i >= bl ? sm.u.hist[hi - i] : 0u;
           sum += c[i];
         }
         uint32_t tot;
@@ -663,7 +695,7 @@ __global__ void __launch_bounds__(BLOCK)
         for (int i = 0; i < PER; ++i) {
           const int b = hi - i;
           run += c[i];
-          if (b >= blo) {
+          if (b >= bl) {
             __hip_atomic_store(&mine[b], run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (c[i]) atomic_add_agent_nr(&gh[b], c[i]);
           }
@@ -676,7 +708,7 @@ __global__ void __launch_bounds__(BLOCK)
 #pragma unroll
         for (int i = 0; i < BPT; ++i) {
           const int b = t + i * BLOCK;
-          r[i] = b >= blo ? load_agent(&gh[b]) : 0u;
+          r[i] = b >= bl ? load_agent(&gh[b]) : 0u;
         }
 #pragma unroll
         for (int i = 0; i < BPT; ++i) sm.u.hist[t + i * BLOCK] = r[i];
@@ -689,9 +721,79 @@ __global__ void __launch_bounds__(BLOCK)
       // Merged counts below K (the sample's floor lay above the K-th value)
       // or a crowded crossing bin: the row's workgroups take the rescue
       // together.
-      path = cr.b < 0 ? 4 : (cr.m > (uint32_t)kSingleCap ? 3 : 1);
-    }
+      return cr.b < 0 ? 4 : (cr.m > (uint32_t)kSingleCap ? 3 : 1);
+    };
     if (path == 1) {
+      path = verify(blo, sf->hist);
+      // Two failures get a second counting round, merged into the digit rows
+      // (zero at rest), rather than the radix rescue:
+      //  * merged counts short of K: the floor lay above the K-th value (a
+      //    sample that met a stretch of high scores the rest of the row does
+      //    not share) -- count again with no floor;
+      //  * the crossing bin is the top one, over the cap: scores above the
+      //    sample's maximum (peaks the sample missed) piled up there -- count
+      //    again over [that bin's lower edge, the row's maximum], only the
+      //    scores at or above the edge.  The row's maximum is merged through
+      //    the slot header (an atomic max of order-preserving keys).
+      bool retry = path == 4;
+      if (path == 3 && cr.b == kBins - 1) {
+        float mx = -__builtin_inff();
+        each([&](int j, int q, bool) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) mx = fmaxf(mx, v[j][e]);  // NaN markers drop out
+        });
+        float mn = mx;
+        wave_minmax(mn, mx);
+        if (l == 0) sm.hmax[w] = mx;
+        if (w == 0) {
+          const float e = bin_edge(kBins - 1, bm);
+          if (l == 0) sm.thr[0] = e;
+        }
+        __syncthreads();
+        if (t == 0) {
+          float pm = sm.hmax[0];
+          for (int i = 1; i < W; ++i) pm = fmaxf(pm, sm.hmax[i]);
+          if (pm == pm && pm > -__builtin_inff())
+            __hip_atomic_fetch_max(&hdr->cand_cur, fkey(pm), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+        const float lo = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sm.thr[0])));
+        row_barrier(hdr, G, nbar, err);
+        const uint32_t tk = __builtin_amdgcn_readfirstlane(load_agent(&hdr->cand_cur));
+        const float top = tk ? from_key(tk) : -__builtin_inff();
+        const float sc = (float)kBins / (top - lo);
+        const float c0 = -lo * sc;
+        if (__builtin_isfinite(lo) && __builtin_isfinite(top) && top > lo &&
+            __builtin_isfinite(top - lo) && __builtin_isfinite(4.0f * sc) &&
+            __builtin_isfinite(4.0f * c0) && sc > 0.0f) {
+          gmin = lo;
+          gmax = top;
+          bm.gmin = lo;
+          bm.sc = sc;
+          bm.c0 = c0;
+          bm.sc4 = 4.0f * sc;
+          bm.c04 = 4.0f * c0;
+          xfloor = lo;
+          retry = true;
+        }
+      }
+      if (retry) {
+        for (int i = t; i < kBins + 64; i += BLOCK) sm.u.hist[i] = 0u;
+        floor_bin = 0;
+        path = verify(0, &sf->dig[0][0]);
+        if (path == 1) {
+          path = 5;
+        } else {
+          // the rescue merges its digit counts in those rows: every
+          // workgroup has read them; back to zero, then on
+          row_barrier(hdr, G, nbar, err);
+          for (int i = t; i < 8 * 256; i += BLOCK)
+            __hip_atomic_store(&sf->dig[0][0] + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          row_barrier(hdr, G, nbar, err);
+        }
+      }
+    }
+    if (path == 1 || path == 5) {
       // ---- compaction (a6) --------------------------------------------------
       // Waves 0 and 1 find the edges of b* and b* + 1; wave 2 sums, over the
       // workgroups before this one, their winners (scores in bins > b*) and
@@ -700,7 +802,7 @@ __global__ void __launch_bounds__(BLOCK)
       // from the second.
       if (w < 2) {
         const float e = bin_edge(cr.b + w, bm);
-        if (l == 0) sm.thr[w] = e;
+        if (l == 0) sm.thr[w] = w == 0 ? fmaxf(e, xfloor) : e;
       } else if (w == 2) {
         uint32_t s0 = 0u, s1 = 0u;
         if (l < g) {
@@ -815,7 +917,7 @@ __global__ void __launch_bounds__(BLOCK)
         }
       }
       rest_slot(sf, t, BLOCK);
-      put_stats(1, (int)cr.m, (int)cr.above, cr.b);
+      put_stats(path, (int)cr.m, (int)cr.above, cr.b);
       return;
     }
   }

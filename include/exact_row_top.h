@@ -156,8 +156,10 @@ int topk_decode_varlen(const float* logits, int64_t row_stride, const int32_t* k
  *      returns them).  NULL = no hints (the calls then equal topk_decode_v /
  *      topk_decode_varlen).
  * The result is the same exact selection as without hints, whatever the
- * hints hold.  Hints whose scores give no usable bracket (all invalid, all
- * one position, none above the sample's minimum) fall back to the sample. */
+ * hints hold.  Hints steer the multi-workgroup tier (the bracket's top and
+ * floor); hints whose scores give no usable bracket (all invalid, all one
+ * position) change nothing.  One-workgroup rows do not read them: their
+ * retry takes the row's own maximum. */
 int topk_decode_hinted(const float* logits, int64_t row_stride, const int32_t* n_valid,
                        const int32_t* pre_idx, int64_t pre_idx_stride, int32_t num_rows, int32_t k,
                        int32_t* indices, float* values, uint32_t flags, void* workspace,
@@ -217,9 +219,12 @@ const char* topk_strerror(int status);
  *      exact radix rescue runs on every long row.
  *  row_stats: optional device int32[num_rows][TOPK_STATS_WORDS]; per row:
  *      [0] path (0 short, 1 bracket + refine, 2 rescue: invalid bracket,
- *          3 rescue: crossing bin over the candidate cap (one-workgroup
- *          rows: also counts above the hint floor short of k), 4 rescue:
- *          split row whose counts above its floor fell short of k),
+ *          3 rescue: crossing bin over the candidate cap (after the
+ *          recounts below, where they apply), 5 fast path after a recount:
+ *          a split row whose counts above its floor fell short of k counted
+ *          again with no floor; a one-workgroup row whose crossing bin was
+ *          the crowded top bin counted that bin again up to the row's
+ *          maximum),
  *      [1] m (crossing-bin population, -1 if not computed),
  *      [2] above (count in bins above the crossing bin, -1 if none),
  *      [3] crossing bin index (-1 if none),

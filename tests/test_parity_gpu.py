@@ -66,7 +66,7 @@ def test_tie_heavy_paths(ert):
     log(f"[paths] {dict(zip(kinds, st[:, 0].tolist()))}")
     # sorted rows can defeat the sample's floor estimate (its blocks are runs
     # of equal values); whichever exact path finishes the row, parity holds
-    assert st[kinds.index("quantised64_sorted"), 0] in (1, 3, 4)
+    assert st[kinds.index("quantised64_sorted"), 0] in (1, 3, 5)
 
 
 def _sample_block_starts(nv, k):
@@ -80,8 +80,10 @@ def _sample_block_starts(nv, k):
 def test_sample_seeking_rows_take_the_rescue(ert, k):
     # Rows whose K largest scores sit exactly on the sample's blocks: the
     # sample then over-represents the top, the floor taken from it lies above
-    # the K-th value, the merged counts miss K, and the split tier must finish
-    # the row with the parallel rescue.  The answer is unique (index-exact).
+    # the K-th value and the merged counts miss K; the recount without a
+    # floor puts every other score in the bracket's bottom bin with the
+    # crossing (over the member cap), and the split tier finishes the row
+    # with the parallel rescue.  The answer is unique (index-exact).
     rows, stride = 4, 65536
     nv = [60000, 59999, 60000, 40000]
     w = workloads.random_decode(rows, stride, nv, k, seed=77, dist="normal")
@@ -99,8 +101,59 @@ def test_sample_seeking_rows_take_the_rescue(ert, k):
         got, st = run_gpu(w, stats=True, **kw)
         assert_parity(w, got, want)
         for r in (0, 1):
-            assert st[r, 6] > 1 and st[r, 0] == 4, st[r]
+            assert st[r, 6] > 1 and st[r, 0] == 3 and st[r, 8] == 0, st[r]
             assert sorted(got[r].tolist()) == sorted(want[r].tolist())
+
+
+@pytest.mark.parametrize("k", [512, 1024])
+def test_crossing_in_the_top_bin(ert, k):
+    # More than K (but under the member cap) scores above the sample's
+    # maximum, placed between its blocks: they all clamp into the top bin,
+    # which holds the crossing; its upper edge bounds nothing.  Both tiers.
+    rows, stride = 3, 32768
+    nv = [32768, 30001, 20000]
+    w = workloads.random_decode(rows, stride, nv, k, seed=79, dist="normal")
+    rng = np.random.default_rng(k)
+    for r in range(rows):
+        taken = np.zeros(nv[r], dtype=bool)
+        for a in _sample_block_starts(nv[r], k):
+            taken[a:a + 64] = True
+        pos = rng.choice(np.flatnonzero(~taken), size=k + 100, replace=False)
+        w.logits[r, pos] = (10.0 + rng.random(k + 100)).astype(np.float32)
+    want = oracle.topk_workload(w)
+    for kw in ({"force_wgs_per_row": 1}, {"force_wgs_per_row": 4},
+               {"force_wgs_per_row": 1, "deterministic": True, "sorted": True}):
+        log(f"[top bin] k={k} {kw}")
+        got, st = run_gpu(w, stats=True, **kw)
+        assert_parity(w, got, want)
+        for r in range(rows):
+            assert st[r, 0] in (1, 5) and st[r, 3] == 2047, st[r]
+        if kw.get("sorted"):
+            assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("k", [512, 2048])
+def test_floor_above_kth_recounts_without_a_floor(ert, k):
+    # Peaks on every other sample block: only K/2 of them exist, so the
+    # sample's floor lies above the K-th value and the merged counts miss K;
+    # the split tier counts again with no floor and finishes on the fast
+    # path (row_stats path 5, floor bin 0).
+    rows, stride = 4, 65536
+    nv = [60000, 59999, 65536, 40000]
+    w = workloads.random_decode(rows, stride, nv, k, seed=78, dist="normal")
+    for r in range(3):
+        starts = _sample_block_starts(nv[r], k)[::2]
+        pos = [s + i for s in starts for i in range(64)]
+        w.logits[r, pos] = (10.0 + np.linspace(0.0, 1.0, len(pos))).astype(np.float32)
+    want = oracle.topk_workload(w)
+    for kw in ({}, {"force_wgs_per_row": 4}, {"deterministic": True, "sorted": True}):
+        log(f"[recount] k={k} {kw}")
+        got, st = run_gpu(w, stats=True, **kw)
+        assert_parity(w, got, want)
+        for r in range(3):
+            assert st[r, 6] > 1 and st[r, 0] == 5 and st[r, 8] == 0, st[r]
+        if kw.get("sorted"):
+            assert np.array_equal(got, want)
 
 
 # ---- tiers must agree ------------------------------------------------------------
