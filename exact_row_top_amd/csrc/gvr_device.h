@@ -35,6 +35,14 @@ __device__ __forceinline__ float from_key(uint32_t k) {
 // while the row holds K non-NaN scores.
 __device__ __forceinline__ uint32_t rkey(float x) { return (x == x) ? fkey(x) : 0u; }
 
+// A float pinned to a scalar register: as an operand of a VOP3 instruction it
+// takes the one scalar slot instead of a literal the compiler would otherwise
+// rematerialise into a VGPR before every use.
+__device__ __forceinline__ float sgpr_f32(float x) {
+  asm("" : "+s"(x));
+  return x;
+}
+
 // The bracket's bin map: bin(x) = trunc(clamp(fma(x, sc, c0), 0, kBins - 1))
 // with sc = kBins / (gmax - gmin) and c0 = -gmin * sc, each rounded once per
 // row.  A fused multiply-add is monotone non-decreasing in x, so equal values
@@ -44,6 +52,7 @@ __device__ __forceinline__ uint32_t rkey(float x) { return (x == x) ? fkey(x) : 
 // NaN (outside the contract): they keep the LDS index in range.
 struct BinMap {
   float gmin, sc, c0, sc4, c04;
+  float top4 = sgpr_f32(4.0f * (kBins - 1));  // vbin_off's clamp bound
 };
 __device__ __forceinline__ int vbin(float x, const BinMap& bm) {
   float t = __builtin_fmaf(x, bm.sc, bm.c0);
@@ -52,7 +61,7 @@ __device__ __forceinline__ int vbin(float x, const BinMap& bm) {
 }
 __device__ __forceinline__ uint32_t vbin_off(float x, const BinMap& bm) {
   float t = __builtin_fmaf(x, bm.sc4, bm.c04);
-  t = __builtin_amdgcn_fmed3f(t, 0.0f, (float)(4 * (kBins - 1)));
+  t = __builtin_amdgcn_fmed3f(t, 0.0f, bm.top4);
   return ((uint32_t)(int)t) & (uint32_t)(4 * kBins - 4);
 }
 // LDS histogram word at a byte offset from vbin_off.
@@ -304,6 +313,48 @@ __device__ __forceinline__ void find_crossing(Load&& load, uint32_t target, Cros
     out->total = tot;
   }
   __syncthreads();
+}
+
+// The same crossing over the kBins-word LDS histogram h, found by one wave
+// alone with no workgroup barrier (every wave that calls it gets the same
+// answer, in scalar registers).  Lane l sums the 32 bins
+// [kBins - 32 (l + 1), kBins - 32 l) with eight 16-byte reads, one in flight
+// at a time (the one-workgroup tier's resident row leaves few VGPRs free); a
+// wave prefix sum from the top picks the lane whose range holds the
+// crossing, then 32 lanes read that range one bin each and a second prefix
+// sum picks the bin.  h must be 16-byte aligned and must not change until
+// every calling wave is past its reads: a writer of h waits at a workgroup
+// barrier first.
+__device__ __forceinline__ Cross wave_crossing(const uint32_t* h, uint32_t target) {
+  static_assert(kBins == 64 * 32, "32 bins per lane");
+  const int l = lane_id();
+  const uint4* p = reinterpret_cast<const uint4*>(h + kBins - 32 * (l + 1));
+  uint32_t s = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint4 c = p[i];
+    s += (c.x + c.y) + (c.z + c.w);
+    asm volatile("" ::: "memory");
+  }
+  const uint32_t inc = wave_incl_scan(s);
+  const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+  // (no lane hits when the total is short of the target: lane 0 stands in,
+  // and the result says b = -1; no branch, so no divergent join)
+  const uint64_t hit = __ballot(inc - s < target && inc >= target);
+  const int f = hit ? (int)__builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit) - 1) : 0;
+  const uint32_t exf = (uint32_t)__builtin_amdgcn_readlane((int)(inc - s), f);
+  const int top = kBins - 1 - 32 * f;  // the highest bin of lane f's range
+  const uint32_t c = l < 32 ? h[top - l] : 0u;
+  const uint32_t inc2 = exf + wave_incl_scan(c);
+  const uint64_t hit2 = __ballot(l < 32 && inc2 - c < target && inc2 >= target);
+  const int g = hit2 ? (int)__builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit2) - 1) : 0;
+  const bool ok = tot >= target;
+  Cross r;
+  r.total = tot;
+  r.b = ok ? top - g : -1;
+  r.above = ok ? (uint32_t)__builtin_amdgcn_readlane((int)(inc2 - c), g) : tot;
+  r.m = ok ? (uint32_t)__builtin_amdgcn_readlane((int)c, g) : 0u;
+  return r;
 }
 
 // Smallest score x (IEEE order over [-inf, +inf]) with vbin(x) >= b, so that

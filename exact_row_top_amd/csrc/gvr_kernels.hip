@@ -584,8 +584,7 @@ __global__ void __launch_bounds__(BLOCK)
       const float lam = (float)K * (float)K / (float)nv;
       const float rl = lam + 4.0f * sqrtf(lam) + 8.0f;
       const uint32_t rlow = rl >= (float)K ? (uint32_t)K : (uint32_t)rl;
-      find_crossing<kBins, BLOCK>([&](int b) { return sm.u.hist[b]; }, rlow, &sm.cross, sm.scan);
-      const Cross sc0 = read_cross(&sm.cross);
+      const Cross sc0 = wave_crossing(sm.u.hist, rlow);
       blo = sc0.b > 0 ? sc0.b : 0;
       if (hint_ok) {
         // Hint-guided floor: the previous step's top-K mostly stays above
@@ -599,11 +598,7 @@ __global__ void __launch_bounds__(BLOCK)
         if (bh < blo) {
           const float ru = lam + 8.0f * sqrtf(lam) + 16.0f;
           int bup = -1;
-          if (ru < (float)K) {
-            find_crossing<kBins, BLOCK>([&](int b) { return sm.u.hist[b]; }, (uint32_t)ru,
-                                        &sm.cross, sm.scan);
-            bup = read_cross(&sm.cross).b;
-          }
+          if (ru < (float)K) bup = wave_crossing(sm.u.hist, (uint32_t)ru).b;
           if (bh >= bup) blo = bh;
         }
       }
@@ -620,13 +615,24 @@ __global__ void __launch_bounds__(BLOCK)
       // can share a bin on a smooth stretch of the row without the row being
       // crowded.
       const float crowded = fmaxf(2.0f * (float)kSingleCap * (float)K / (float)nv, 32.0f);
-      for (int i = t; i < kBins + 64; i += BLOCK) {
-        if (i < kBins && i >= blo) {
-          const uint32_t c = sm.u.hist[i];
-          if (c >= 8u) sm.bc[3] = 1u;
-          if ((float)c >= crowded) sm.ctr[3] = 1u;
+      __syncthreads();  // every wave has read the sample's counts
+      {
+        // four bins per read; each thread then clears what it read
+        uint32_t mx = 0u;
+        for (int i4 = t; i4 < (kBins + 64) / 4; i4 += BLOCK) {
+          uint4* p4 = reinterpret_cast<uint4*>(sm.u.hist) + i4;
+          if (i4 < kBins / 4) {
+            const uint4 c = *p4;
+            const int b = 4 * i4;
+            mx = max(mx, b >= blo ? c.x : 0u);
+            mx = max(mx, b + 1 >= blo ? c.y : 0u);
+            mx = max(mx, b + 2 >= blo ? c.z : 0u);
+            mx = max(mx, b + 3 >= blo ? c.w : 0u);
+          }
+          *p4 = uint4{0u, 0u, 0u, 0u};
         }
-        sm.u.hist[i] = 0u;
+        if (mx >= 8u) sm.bc[3] = 1u;
+        if ((float)mx >= crowded) sm.ctr[3] = 1u;
       }
       __syncthreads();
       path = sm.ctr[3] ? 3 : 1;
@@ -715,9 +721,7 @@ __global__ void __launch_bounds__(BLOCK)
       }
       __syncthreads();
       // ---- crossing bin (a5), the same in every workgroup of the row -----
-      find_crossing<kBins, BLOCK>([&](int b) { return sm.u.hist[b]; }, (uint32_t)K, &sm.cross,
-                                  sm.scan);
-      cr = read_cross(&sm.cross);
+      cr = wave_crossing(sm.u.hist, (uint32_t)K);
       // Merged counts below K (the sample's floor lay above the K-th value)
       // or a crowded crossing bin: the row's workgroups take the rescue
       // together.
@@ -778,6 +782,7 @@ __global__ void __launch_bounds__(BLOCK)
         }
       }
       if (retry) {
+        __syncthreads();  // every wave has read the merged counts
         for (int i = t; i < kBins + 64; i += BLOCK) sm.u.hist[i] = 0u;
         floor_bin = 0;
         path = verify(0, &sf->dig[0][0]);
