@@ -448,9 +448,13 @@ __device__ __forceinline__ bool finish_slot(SlotHeader* hdr, int G, uint32_t* bc
   return *bc == (uint32_t)(G - 1);
 }
 
-__device__ __forceinline__ void rest_slot(SlotFixed* sf, int t, int block) {
-  for (int i = t; i < 8 * 256; i += block) (&sf->dig[0][0])[i] = 0u;
-  for (int i = t; i < kBins; i += block) sf->hist[i] = 0u;
+// Return a row's slot to its resting state (all zero): the histogram from bin
+// hist_lo up (no round adds below its floor), the digit rows when `dig`, and
+// the header.
+__device__ __forceinline__ void rest_slot(SlotFixed* sf, int t, int block, int hist_lo, bool dig) {
+  if (dig)
+    for (int i = t; i < 8 * 256; i += block) (&sf->dig[0][0])[i] = 0u;
+  for (int i = hist_lo + t; i < kBins; i += block) sf->hist[i] = 0u;
   if (t == 0) {
     sf->hdr.bar_count = 0u;
     sf->hdr.win_cur = 0u;

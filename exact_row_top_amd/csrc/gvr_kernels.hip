@@ -854,20 +854,6 @@ __global__ void __launch_bounds__(BLOCK)
         ncand += __popc(cb[i]);
       }
       const uint32_t ex = wave_offsets((ncand << 16) | nwin, &sm.ctr[2]);
-      {
-        uint32_t wpos = sm.bc[0] + (ex & 0xFFFFu);
-#pragma unroll
-        for (int d = 0; d < NW; ++d) {
-          uint32_t bits = wb[d];
-          while (bits) {
-            const int i = d * 32 + __builtin_ctz(bits);
-            bits &= bits - 1u;
-            const int q = q0 + t + (i >> 2) * BLOCK;
-            if (wpos < above) out[wpos] = (q << 2) + (i & 3) - lead;
-            ++wpos;
-          }
-        }
-      }
       uint64_t* list = reinterpret_cast<uint64_t*>(s_pair);
       {
         uint32_t cpos = sm.bc[1] + (ex >> 16);
@@ -894,7 +880,25 @@ __global__ void __launch_bounds__(BLOCK)
         });
       }
       // ---- refine (a7): the row's last workgroup picks `need` members -----
-      if (!finish_slot(hdr, G, &sm.bc[2])) return;
+      // The done count waits for the member list only: the winners go out
+      // after it (nothing reads them in this launch), so their stores overlap
+      // its round trip and the last workgroup's refine.
+      const bool last = finish_slot(hdr, G, &sm.bc[2]);
+      {
+        uint32_t wpos = sm.bc[0] + (ex & 0xFFFFu);
+#pragma unroll
+        for (int d = 0; d < NW; ++d) {
+          uint32_t bits = wb[d];
+          while (bits) {
+            const int i = d * 32 + __builtin_ctz(bits);
+            bits &= bits - 1u;
+            const int q = q0 + t + (i >> 2) * BLOCK;
+            if (wpos < above) out[wpos] = (q << 2) + (i & 3) - lead;
+            ++wpos;
+          }
+        }
+      }
+      if (!last) return;
       if (!direct) {
         for (uint32_t i0 = 0; i0 < m; i0 += 4 * BLOCK) {
           uint64_t r[4];
@@ -921,7 +925,9 @@ __global__ void __launch_bounds__(BLOCK)
                              (uint32_t)K, sm.dh, &sm.cross, sm.scan, sm.ctr, nbar);
         }
       }
-      rest_slot(sf, t, BLOCK);
+      // back to zero: the histogram bins the first round added to, and the
+      // digit rows when a second round used them
+      rest_slot(sf, t, BLOCK, blo, path == 5);
       put_stats(path, (int)cr.m, (int)cr.above, cr.b);
       return;
     }
@@ -1003,7 +1009,7 @@ __global__ void __launch_bounds__(BLOCK)
     bool last = true;
     if (SPLIT) {
       last = finish_slot(hdr, G, &sm.bc[2]);
-      if (last) rest_slot(sf, t, BLOCK);
+      if (last) rest_slot(sf, t, BLOCK, 0, true);
     }
     if (last)
       put_stats(path, bracket_ok && !SPLIT ? (int)cr.m : -1, bracket_ok && !SPLIT ? (int)cr.above : -1,
