@@ -64,6 +64,48 @@ __device__ __forceinline__ uint32_t vbin_off(float x, const BinMap& bm) {
   t = __builtin_amdgcn_fmed3f(t, 0.0f, bm.top4);
   return ((uint32_t)(int)t) & (uint32_t)(4 * kBins - 4);
 }
+// One lane's float4 group against the crossing bin's edges [xlo, xhi) (both
+// uniform): its four winner bits (x >= xhi) are shifted into wacc and its
+// four member bits (xlo <= x < xhi) into cacc, each by add-with-carry
+// doublings (acc = 2 acc + bit: the group's first score lands in the highest
+// of the four new bits).  NaN compares false both ways.  Every scalar pair a
+// doubling reads as its carry-in was written four or more instructions
+// earlier.  The member masks come from scalar and-nots inside the block,
+// which write SCC: declared clobbered, so no compare the compiler made
+// before the block is read after it.  Compared with a compare and a select
+// per bit, this takes two VALU instructions per score and threshold and no
+// wait states.
+__device__ __forceinline__ void group_bits(const f4& x, float xlo, float xhi, uint32_t& wacc,
+                                           uint32_t& cacc) {
+  uint64_t h0, h1, h2, h3, g0, g1, g2, g3, cy;
+  asm("v_cmp_ge_f32_e64 %[h0], %[x0], %[hi]\n\t"
+      "v_cmp_ge_f32_e64 %[h1], %[x1], %[hi]\n\t"
+      "v_cmp_ge_f32_e64 %[h2], %[x2], %[hi]\n\t"
+      "v_cmp_ge_f32_e64 %[h3], %[x3], %[hi]\n\t"
+      "v_cmp_ge_f32_e64 %[g0], %[x0], %[lo]\n\t"
+      "v_cmp_ge_f32_e64 %[g1], %[x1], %[lo]\n\t"
+      "v_cmp_ge_f32_e64 %[g2], %[x2], %[lo]\n\t"
+      "v_cmp_ge_f32_e64 %[g3], %[x3], %[lo]\n\t"
+      "s_andn2_b64 %[g0], %[g0], %[h0]\n\t"
+      "s_andn2_b64 %[g1], %[g1], %[h1]\n\t"
+      "s_andn2_b64 %[g2], %[g2], %[h2]\n\t"
+      "s_andn2_b64 %[g3], %[g3], %[h3]\n\t"
+      "v_addc_co_u32_e64 %[w], %[cy], %[w], %[w], %[h0]\n\t"
+      "v_addc_co_u32_e64 %[w], %[cy], %[w], %[w], %[h1]\n\t"
+      "v_addc_co_u32_e64 %[w], %[cy], %[w], %[w], %[h2]\n\t"
+      "v_addc_co_u32_e64 %[w], %[cy], %[w], %[w], %[h3]\n\t"
+      "v_addc_co_u32_e64 %[c], %[cy], %[c], %[c], %[g0]\n\t"
+      "v_addc_co_u32_e64 %[c], %[cy], %[c], %[c], %[g1]\n\t"
+      "v_addc_co_u32_e64 %[c], %[cy], %[c], %[c], %[g2]\n\t"
+      "v_addc_co_u32_e64 %[c], %[cy], %[c], %[c], %[g3]"
+      : [w] "+v"(wacc), [c] "+v"(cacc), [h0] "=&s"(h0), [h1] "=&s"(h1), [h2] "=&s"(h2),
+        [h3] "=&s"(h3), [g0] "=&s"(g0), [g1] "=&s"(g1), [g2] "=&s"(g2), [g3] "=&s"(g3),
+        [cy] "=&s"(cy)
+      : [x0] "v"(x[0]), [x1] "v"(x[1]), [x2] "v"(x[2]), [x3] "v"(x[3]), [hi] "s"(xhi),
+        [lo] "s"(xlo)
+      : "scc");
+}
+
 // LDS histogram word at a byte offset from vbin_off.
 __device__ __forceinline__ uint32_t* hword(uint32_t* h, uint32_t off) {
   return reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(h) + off);
