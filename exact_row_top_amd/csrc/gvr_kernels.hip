@@ -523,6 +523,8 @@ __global__ void __launch_bounds__(BLOCK)
           while (bits) {
             const int i = top - __builtin_ctz(bits);
             bits &= bits - 1u;
+            // (the slot is clamped, not tested: the winners number exactly
+            // cr.above <= K)
             out[min(wpos, (uint32_t)K - 1u)] = base + (i & ~3) * BLOCK + (i & 3);
             ++wpos;
           }
@@ -826,22 +828,18 @@ __global__ void __launch_bounds__(BLOCK)
       uint32_t wb[NW], cb[NW];
 #pragma unroll
       for (int i = 0; i < NW; ++i) wb[i] = cb[i] = 0u;
+      int ngrp = 0;  // groups this wave visited (uniform)
       {
-        const float xlo = sm.thr[0], xhi = sm.thr[1];
+        const float xlo = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sm.thr[0])));
+        const float xhi = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sm.thr[1])));
         each([&](int j, int q, bool) {
-          // one nibble per mask and group (inline bit constants), shifted in
-          uint32_t nw = 0u, ng = 0u;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float x = v[j][e];
-            nw |= (x >= xhi) ? (1u << e) : 0u;
-            ng |= (x >= xlo) ? (1u << e) : 0u;
-          }
-          const int sh = (j * 4) & 31;
-          wb[(j * 4) >> 5] |= nw << sh;
-          cb[(j * 4) >> 5] |= (ng & ~nw) << sh;
+          group_bits(v[j], xlo, xhi, wb[j >> 3], cb[j >> 3]);
+          ngrp = j + 1;
         });
       }
+      // word d holds groups 8d .. 8d + 7, nd bits shifted in: bit p is this
+      // thread's score i = 32 d + nd - 1 - p (group i / 4, lane i % 4)
+      auto nbits = [&](int d) { return 4 * min(max(ngrp - 8 * d, 0), 8); };
       uint32_t nwin = 0, ncand = 0;
 #pragma unroll
       for (int i = 0; i < NW; ++i) {
@@ -853,11 +851,13 @@ __global__ void __launch_bounds__(BLOCK)
       {
         uint32_t cpos = sm.bc[1] + (ex >> 16);
         each([&](int j, int q, bool) {
-          const uint32_t cq = (cb[(j * 4) >> 5] >> ((j * 4) & 31)) & 0xFu;
+          const int d = j >> 3;
+          const int sh = nbits(d) - 4 - 4 * (j - 8 * d);  // the group's lowest bit (score 3)
+          const uint32_t cq = (cb[d] >> sh) & 0xFu;
           if (__any(cq != 0u)) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const bool c = (cq >> e) & 1u;
+              const bool c = (cq >> (3 - e)) & 1u;
               if (c && cpos < m) {
                 const int32_t idx = (q << 2) + e - lead;
                 if (direct) {
@@ -881,14 +881,17 @@ __global__ void __launch_bounds__(BLOCK)
       const bool last = finish_slot(hdr, G, &sm.bc[2]);
       {
         uint32_t wpos = sm.bc[0] + (ex & 0xFFFFu);
+        const int base = ((q0 + t) << 2) - lead;
 #pragma unroll
         for (int d = 0; d < NW; ++d) {
+          const int top = 32 * d + nbits(d) - 1;
           uint32_t bits = wb[d];
           while (bits) {
-            const int i = d * 32 + __builtin_ctz(bits);
+            const int i = top - __builtin_ctz(bits);
             bits &= bits - 1u;
-            const int q = q0 + t + (i >> 2) * BLOCK;
-            if (wpos < above) out[wpos] = (q << 2) + (i & 3) - lead;
+            // (the slot is clamped, not tested: the row's winners number
+            // exactly `above` <= K)
+            out[min(wpos, (uint32_t)K - 1u)] = base + (i & ~3) * BLOCK + (i & 3);
             ++wpos;
           }
         }
