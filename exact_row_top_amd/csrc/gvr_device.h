@@ -357,6 +357,68 @@ __device__ __forceinline__ void find_crossing(Load&& load, uint32_t target, Cros
   __syncthreads();
 }
 
+// The crossing over the kBins-word LDS histogram h with a single workgroup
+// barrier: thread t sums its kBins / BLOCK bins from the top, a wave prefix
+// sum plus the waves' totals (through scan_sm, after the barrier) give every
+// wave the wave whose bins hold the crossing; each wave then sums that
+// wave's per-thread bins again, picks the thread, and 32 or fewer lanes read
+// its bins one each to pick the bin.  Every wave returns the same answer in
+// scalar registers.  h and scan_sm must not change until every wave is past
+// its reads (a writer waits at a workgroup barrier first).
+template <int BLOCK>
+__device__ __forceinline__ Cross crossing_1sync(const uint32_t* h, uint32_t target,
+                                                uint32_t* scan_sm) {
+  constexpr int PER = kBins / BLOCK;
+  constexpr int W = BLOCK / 64;
+  static_assert(PER * BLOCK == kBins && PER <= 64, "bins per thread");
+  const int l = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  auto owner_sum = [&](int owner) {
+    const int hi = kBins - 1 - owner * PER;
+    uint32_t s = 0u;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) s += h[hi - i];
+    return s;
+  };
+  const uint32_t s = owner_sum((int)threadIdx.x);
+  const uint32_t inc = wave_incl_scan(s);
+  if (l == 63) scan_sm[w] = inc;
+  __syncthreads();
+  uint32_t run = 0u, exw = 0u;
+  int cw = -1;
+#pragma unroll
+  for (int i = 0; i < W; ++i) {
+    const uint32_t c = (uint32_t)__builtin_amdgcn_readfirstlane((int)scan_sm[i]);
+    if (cw < 0 && run + c >= target) {
+      cw = i;
+      exw = run;
+    }
+    run += c;
+  }
+  Cross r;
+  r.total = run;
+  if (cw < 0) {
+    r.b = -1;
+    r.above = run;
+    r.m = 0u;
+    return r;
+  }
+  const uint32_t s2 = owner_sum(cw * 64 + l);
+  const uint32_t inc2 = exw + wave_incl_scan(s2);
+  const uint64_t hit = __ballot(inc2 - s2 < target && inc2 >= target);
+  const int f = (int)__builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit) - 1);
+  const uint32_t ex = (uint32_t)__builtin_amdgcn_readlane((int)(inc2 - s2), f);
+  const int hi = kBins - 1 - (cw * 64 + f) * PER;
+  const uint32_t c = l < PER ? h[hi - l] : 0u;
+  const uint32_t inc3 = ex + wave_incl_scan(c);
+  const uint64_t hit2 = __ballot(l < PER && inc3 - c < target && inc3 >= target);
+  const int g = (int)__builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit2) - 1);
+  r.b = hi - g;
+  r.above = (uint32_t)__builtin_amdgcn_readlane((int)(inc3 - c), g);
+  r.m = (uint32_t)__builtin_amdgcn_readlane((int)c, g);
+  return r;
+}
+
 // The same crossing over the kBins-word LDS histogram h, found by one wave
 // alone with no workgroup barrier (every wave that calls it gets the same
 // answer, in scalar registers).  Lane l sums the 32 bins

@@ -429,9 +429,7 @@ __global__ void __launch_bounds__(BLOCK)
           });
         }
         __syncthreads();
-        find_crossing<kBins, BLOCK>([&](int b) { return sm.u.hist[b]; }, (uint32_t)K, &sm.cross,
-                                    sm.scan);
-        cr = read_cross(&sm.cross);
+        cr = crossing_1sync<BLOCK>(sm.u.hist, (uint32_t)K, sm.scan);
         path = (cr.b >= 0 && cr.m <= (uint32_t)kSingleCap) ? 1 : 3;
       };
       verify(false);
@@ -530,7 +528,8 @@ __global__ void __launch_bounds__(BLOCK)
           }
         }
       }
-      {
+      // (a wave without members skips the pass)
+      if (__any(ncand != 0u)) {
         uint32_t cpos = ex >> 16;
         each([&](int j, int q, bool) {
           const int d = j >> 3;
@@ -848,7 +847,7 @@ __global__ void __launch_bounds__(BLOCK)
       }
       const uint32_t ex = wave_offsets((ncand << 16) | nwin, &sm.ctr[2]);
       uint64_t* list = reinterpret_cast<uint64_t*>(s_pair);
-      {
+      if (__any(ncand != 0u)) {
         uint32_t cpos = sm.bc[1] + (ex >> 16);
         each([&](int j, int q, bool) {
           const int d = j >> 3;
