@@ -419,48 +419,6 @@ __device__ __forceinline__ Cross crossing_1sync(const uint32_t* h, uint32_t targ
   return r;
 }
 
-// The same crossing over the kBins-word LDS histogram h, found by one wave
-// alone with no workgroup barrier (every wave that calls it gets the same
-// answer, in scalar registers).  Lane l sums the 32 bins
-// [kBins - 32 (l + 1), kBins - 32 l) with eight 16-byte reads, one in flight
-// at a time (the one-workgroup tier's resident row leaves few VGPRs free); a
-// wave prefix sum from the top picks the lane whose range holds the
-// crossing, then 32 lanes read that range one bin each and a second prefix
-// sum picks the bin.  h must be 16-byte aligned and must not change until
-// every calling wave is past its reads: a writer of h waits at a workgroup
-// barrier first.
-__device__ __forceinline__ Cross wave_crossing(const uint32_t* h, uint32_t target) {
-  static_assert(kBins == 64 * 32, "32 bins per lane");
-  const int l = lane_id();
-  const uint4* p = reinterpret_cast<const uint4*>(h + kBins - 32 * (l + 1));
-  uint32_t s = 0u;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint4 c = p[i];
-    s += (c.x + c.y) + (c.z + c.w);
-    asm volatile("" ::: "memory");
-  }
-  const uint32_t inc = wave_incl_scan(s);
-  const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
-  // (no lane hits when the total is short of the target: lane 0 stands in,
-  // and the result says b = -1; no branch, so no divergent join)
-  const uint64_t hit = __ballot(inc - s < target && inc >= target);
-  const int f = hit ? (int)__builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit) - 1) : 0;
-  const uint32_t exf = (uint32_t)__builtin_amdgcn_readlane((int)(inc - s), f);
-  const int top = kBins - 1 - 32 * f;  // the highest bin of lane f's range
-  const uint32_t c = l < 32 ? h[top - l] : 0u;
-  const uint32_t inc2 = exf + wave_incl_scan(c);
-  const uint64_t hit2 = __ballot(l < 32 && inc2 - c < target && inc2 >= target);
-  const int g = hit2 ? (int)__builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit2) - 1) : 0;
-  const bool ok = tot >= target;
-  Cross r;
-  r.total = tot;
-  r.b = ok ? top - g : -1;
-  r.above = ok ? (uint32_t)__builtin_amdgcn_readlane((int)(inc2 - c), g) : tot;
-  r.m = ok ? (uint32_t)__builtin_amdgcn_readlane((int)c, g) : 0u;
-  return r;
-}
-
 // Smallest score x (IEEE order over [-inf, +inf]) with vbin(x) >= b, so that
 // for every non-NaN x: vbin(x) >= b  <=>  x >= edge.  vbin is monotone in x,
 // so the set is an up-set.  The 64 lanes first probe the keys around the

@@ -580,7 +580,7 @@ __global__ void __launch_bounds__(BLOCK)
       const float lam = (float)K * (float)K / (float)nv;
       const float rl = lam + 4.0f * sqrtf(lam) + 8.0f;
       const uint32_t rlow = rl >= (float)K ? (uint32_t)K : (uint32_t)rl;
-      const Cross sc0 = wave_crossing(sm.u.hist, rlow);
+      const Cross sc0 = crossing_1sync<BLOCK>(sm.u.hist, rlow, sm.scan);
       blo = sc0.b > 0 ? sc0.b : 0;
       if (hint_ok) {
         // Hint-guided floor: the previous step's top-K mostly stays above
@@ -594,7 +594,7 @@ __global__ void __launch_bounds__(BLOCK)
         if (bh < blo) {
           const float ru = lam + 8.0f * sqrtf(lam) + 16.0f;
           int bup = -1;
-          if (ru < (float)K) bup = wave_crossing(sm.u.hist, (uint32_t)ru).b;
+          if (ru < (float)K) bup = crossing_1sync<BLOCK>(sm.u.hist, (uint32_t)ru, sm.scan).b;
           if (bh >= bup) blo = bh;
         }
       }
@@ -717,7 +717,7 @@ __global__ void __launch_bounds__(BLOCK)
       }
       __syncthreads();
       // ---- crossing bin (a5), the same in every workgroup of the row -----
-      cr = wave_crossing(sm.u.hist, (uint32_t)K);
+      cr = crossing_1sync<BLOCK>(sm.u.hist, (uint32_t)K, sm.scan);
       // Merged counts below K (the sample's floor lay above the K-th value)
       // or a crowded crossing bin: the row's workgroups take the rescue
       // together.
