@@ -32,9 +32,12 @@ struct Variant {
 // waves per row keep the per-row fixed work (sample, scans, crossing, edges,
 // refine) small next to the per-score work.
 constexpr Variant kSingleVariants[] = {{256, 8}, {256, 17}, {512, 9}, {1024, 9}};
-// G workgroups per row, each holding 1/G of the row.
-constexpr int kSplitBlock = 256;
-constexpr int kSplitQpt[] = {4, 8, 17};
+// G workgroups per row, each holding 1/G of the row; in order of capacity
+// (the planner takes the first that holds a part).  The largest part runs
+// 512 threads: a few long rows leave few workgroups per compute unit, and
+// eight waves each hide more of a part's latency than four.
+constexpr Variant kSplitVariants[] = {{256, 4}, {256, 8}, {512, 9}};
+constexpr int kNumSplit = 3;
 
 constexpr int kMaxWgsPerRow = 64;
 constexpr int kMaxSlots = 256;  // split rows per launch (workspace slots)

@@ -1026,13 +1026,10 @@ static const void* kernel_ptr() {
 template <int K>
 static const void* pick(int block, int qpt, bool split) {
   if (split) {
-    if (block != kSplitBlock) return nullptr;
-    switch (qpt) {
-      case 4: return kernel_ptr<K, 4, kSplitBlock, true>();
-      case 8: return kernel_ptr<K, 8, kSplitBlock, true>();
-      case 17: return kernel_ptr<K, 17, kSplitBlock, true>();
-      default: return nullptr;
-    }
+    if (block == 256 && qpt == 4) return kernel_ptr<K, 4, 256, true>();
+    if (block == 256 && qpt == 8) return kernel_ptr<K, 8, 256, true>();
+    if (block == 512 && qpt == 9) return kernel_ptr<K, 9, 512, true>();
+    return nullptr;
   }
   if (block == 256 && qpt == 8) return kernel_ptr<K, 8, 256, false>();
   if (block == 256 && qpt == 17) return kernel_ptr<K, 17, 256, false>();

@@ -70,11 +70,13 @@ int make_plan(int32_t num_rows, int64_t env_len, int32_t k, int32_t force_g, int
     G = 1;  // rows short enough for the smallest workgroup: splitting costs more
             // in cross-workgroup latency than it gains in bandwidth
   } else {
-    const int64_t part_max = (int64_t)kSplitBlock * kSplitQpt[2];
+    const int64_t part_max =
+        (int64_t)kSplitVariants[kNumSplit - 1].block * kSplitVariants[kNumSplit - 1].qpt;
     const int64_t g_min = (Qmax + part_max - 1) / part_max;
     const int64_t g_fill = (kFillUnits + num_rows - 1) / (num_rows > 0 ? num_rows : 1);
     // never parts below 4 groups per thread
-    const int64_t g_useful = (Qmax + (int64_t)kSplitBlock * 4 - 1) / ((int64_t)kSplitBlock * 4);
+    const int64_t part_min = (int64_t)kSplitVariants[0].block * kSplitVariants[0].qpt;
+    const int64_t g_useful = (Qmax + part_min - 1) / part_min;
     int64_t gg = g_fill < g_useful ? g_fill : g_useful;
     if (gg < g_min) gg = g_min;
     if (gg < 1) gg = 1;
@@ -95,14 +97,15 @@ int make_plan(int32_t num_rows, int64_t env_len, int32_t k, int32_t force_g, int
     p.cap = kSingleCap;
   } else {
     const int64_t per_part = (Qmax + G - 1) / G;
-    int qpt = 0;
-    for (int q : kSplitQpt)
-      if ((int64_t)kSplitBlock * q >= per_part) {
-        qpt = q;
+    int qpt = 0, block = 0;
+    for (const Variant& sv : kSplitVariants)
+      if ((int64_t)sv.block * sv.qpt >= per_part) {
+        qpt = sv.qpt;
+        block = sv.block;
         break;
       }
     if (qpt == 0) return TOPK_EINVAL;  // forced G too small for this row length
-    p.block = kSplitBlock;
+    p.block = block;
     p.qpt = qpt;
     int64_t rpl = capacity / G;
     if (rpl > kMaxSlots) rpl = kMaxSlots;
@@ -166,8 +169,8 @@ std::mutex g_mu;
 
 int kidx(int k) { return k == 512 ? 0 : (k == 1024 ? 1 : 2); }
 int qidx(int q) {
-  for (int i = 0; i < 3; ++i)
-    if (kSplitQpt[i] == q) return i;
+  for (int i = 0; i < kNumSplit; ++i)
+    if (kSplitVariants[i].qpt == q) return i;
   return 0;
 }
 
@@ -184,9 +187,10 @@ int device_info(DevInfo** out, int* dev_out) {
     for (int ki = 0; ki < 3; ++ki)
       for (int qi = 0; qi < 3; ++qi) {
         const int ks[3] = {512, 1024, 2048};
-        const void* f = gvr_kernel(ks[ki], kSplitBlock, kSplitQpt[qi], true);
+        const int blk = kSplitVariants[qi].block;
+        const void* f = gvr_kernel(ks[ki], blk, kSplitVariants[qi].qpt, true);
         int nb = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, f, kSplitBlock, 0) != hipSuccess)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, f, blk, 0) != hipSuccess)
           nb = 0;
         d.occ_api[ki][qi] = nb;
         // Residency from the kernel's own resources and the gfx950 compute
@@ -199,7 +203,7 @@ int device_info(DevInfo** out, int* dev_out) {
         if (hipFuncGetAttributes(&at, f) == hipSuccess) {
           const int v = at.numRegs > 0 ? ((at.numRegs + 7) / 8) * 8 : 512;
           const int waves_simd = std::min(8, 512 / v);
-          const int wg_waves = kSplitBlock / 64;
+          const int wg_waves = blk / 64;
           const int by_vgpr = (4 * waves_simd) / wg_waves;
           const int lds = (int)at.sharedSizeBytes;
           const int by_lds = lds > 0 ? (160 * 1024) / lds : 64;

@@ -122,8 +122,8 @@ def test_plans_for_the_workloads():
     for rows, stride, k in ((64, 131072, 2048), (1, 131072, 512), (8, 131072, 512),
                             (8, 262144, 2048)):
         p = ert.plan_query(rows, stride, k)
-        assert p["wgs_per_row"] > 1 and p["block"] == 256
-        assert p["wgs_per_row"] * p["quads_per_thread"] * 256 >= (stride + 6) // 4
+        assert p["wgs_per_row"] > 1 and p["block"] in (256, 512)
+        assert p["wgs_per_row"] * p["quads_per_thread"] * p["block"] >= (stride + 6) // 4
         assert p["cap"] == 2048
     # capacity bounds rows per launch (co-resident split workgroups)
     p = ert.plan_query(64, 131072, 2048, cu_count=16, wgs_per_cu=2)
