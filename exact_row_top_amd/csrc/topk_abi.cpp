@@ -78,6 +78,7 @@ int make_plan(int32_t num_rows, int64_t env_len, int32_t k, int32_t force_g, int
     const int64_t part_min = (int64_t)kSplitVariants[0].block * kSplitVariants[0].qpt;
     const int64_t g_useful = (Qmax + part_min - 1) / part_min;
     int64_t gg = g_fill < g_useful ? g_fill : g_useful;
+    if (gg > kMaxWgsPerRow) gg = kMaxWgsPerRow;  // larger parts then
     if (gg < g_min) gg = g_min;
     if (gg < 1) gg = 1;
     if (gg > kMaxWgsPerRow) return TOPK_EINVAL;  // row longer than the largest plan

@@ -125,6 +125,12 @@ def test_plans_for_the_workloads():
         assert p["wgs_per_row"] > 1 and p["block"] in (256, 512)
         assert p["wgs_per_row"] * p["quads_per_thread"] * p["block"] >= (stride + 6) // 4
         assert p["cap"] == 2048
+    # few rows of 262144: more parts than the split tier allows would be
+    # useful, so the plan takes the most it allows with larger parts
+    for rows, k in ((1, 2048), (7, 512), (2, 1024)):
+        p = ert.plan_query(rows, 262144, k)
+        assert p["wgs_per_row"] == 64
+        assert 64 * p["quads_per_thread"] * p["block"] >= (262144 + 6) // 4
     # capacity bounds rows per launch (co-resident split workgroups)
     p = ert.plan_query(64, 131072, 2048, cu_count=16, wgs_per_cu=2)
     assert p["rows_per_launch"] * p["wgs_per_row"] <= 32 and p["launches"] > 1
@@ -140,7 +146,7 @@ def test_plan_forced_tiers():
     with pytest.raises(ert.TopKError):
         ert.plan_query(8, 4096, 512, force_wgs_per_row=65)
     with pytest.raises(ert.TopKError):
-        ert.plan_query(1, 64 * 17 * 256 * 4 + 64, 512)        # longer than the largest plan
+        ert.plan_query(1, 64 * 9 * 512 * 4 + 64, 512)         # longer than the largest plan
 
 
 def test_output_options_and_varlen_validation():
