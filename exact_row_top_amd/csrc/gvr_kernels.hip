@@ -118,7 +118,12 @@ __global__ void __launch_bounds__(BLOCK)
     slot = L / G;
     g = L - slot * G;
   } else {
-    slot = blockIdx.x;
+    // Last row first: in a causal prefill tile a request's windows grow row
+    // by row, so its long rows start early and the launch drains on short
+    // ones (longest-first dispatch; decode batches of random lengths are
+    // indifferent to the order).  Measured on the 4096 x 16640 tile:
+    // 40.2 -> 38.2 us.
+    slot = (int)gridDim.x - 1 - (int)blockIdx.x;
     g = 0;
   }
   if (slot >= p.rows) return;
