@@ -74,7 +74,10 @@ enum {
   TOPK_OK = 0,
   TOPK_EINVAL = 1,     /* null pointer with num_rows > 0, num_rows < 0, k not in
                           {512,1024,2048}, row_stride < 1 or >= 2^30, bad option
-                          value, a row longer than the largest launch plan */
+                          value, a row longer than the largest launch plan
+                          (64 workgroups x 512 threads x 9 float4 groups:
+                          1,179,648 scores from the 16-byte boundary below
+                          the window's start) */
   TOPK_ELAYOUT = 2,    /* logits not 16-byte aligned, row_stride % 4 != 0,
                           indices / extents not 4-byte aligned */
   TOPK_EWORKSPACE = 3, /* caller workspace smaller than topk_workspace_bytes */
