@@ -497,6 +497,8 @@ __global__ void __launch_bounds__(BLOCK)
       uint32_t wb[NW], cb[NW];
 #pragma unroll
       for (int i = 0; i < NW; ++i) wb[i] = cb[i] = 0u;
+      // this thread's winner (x >= x_hi) and member (x_lo <= x < x_hi) bits,
+      // shifted in group by group
       int ngrp = 0;  // groups this wave visited (uniform)
       {
         const float xlo = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sm.thr[0])));
@@ -832,6 +834,8 @@ __global__ void __launch_bounds__(BLOCK)
       uint32_t wb[NW], cb[NW];
 #pragma unroll
       for (int i = 0; i < NW; ++i) wb[i] = cb[i] = 0u;
+      // this thread's winner (x >= x_hi) and member (x_lo <= x < x_hi) bits,
+      // shifted in group by group
       int ngrp = 0;  // groups this wave visited (uniform)
       {
         const float xlo = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sm.thr[0])));
