@@ -54,6 +54,7 @@ struct alignas(16) BskSmem {
   uint32_t key[kBskMembers];
   int32_t idx[kBskMembers];
   uint32_t dh[256];
+  uint32_t mm[2 * (kBskBlock / 64)];  // per-wave class extremes of a radix level
   uint32_t scan[kBskBlock / 64];
   float rmin[kBskBlock / 64];
   float rmax[kBskBlock / 64];
@@ -355,7 +356,7 @@ __global__ void __launch_bounds__(kBskBlock) topk_blockskip_kernel(const GvrPara
       rank_select<BLOCK>(sm.key, sm.idx, m, need, out, cr.above);
     } else {
       list_select<BLOCK>(sm.key, sm.idx, m, need, p.deterministic != 0, out, cr.above, (uint32_t)K,
-                         sm.dh, &sm.cross, sm.scan, sm.ctr, nbar);
+                         sm.dh, &sm.cross, sm.scan, sm.mm, sm.ctr, nbar);
     }
   } else {
     // ---- radix select inside the crossing region (or the whole row) -------
@@ -382,19 +383,19 @@ __global__ void __launch_bounds__(kBskBlock) topk_blockskip_kernel(const GvrPara
       });
     };
     const uint32_t need = (uint32_t)K - above;
-    const RSel s = radix_select<BLOCK>(iter, need, sm.dh, &sm.cross, sm.scan, nullptr, nullptr, 1,
-                                       nbar, nullptr);
+    const RSel s = radix_select<BLOCK>(iter, need, sm.dh, &sm.cross, sm.scan, sm.mm, nullptr,
+                                       nullptr, nullptr, 1, nbar, nullptr);
     const bool pick = p.deterministic && s.cnt > s.rem;
     RSel s2{0u, 0, 0u, 0u};
     if (pick) {
-      const uint32_t tk = s.thr;  // all four levels ran: one exact key
+      const uint32_t tk = s.thr;  // the select ended on one exact key
       s2 = radix_select<BLOCK>(
           [&](auto&& f) {
             walk([&](float x, int pos) {
               if (in_class(x)) f(rkey(x) == tk ? ~(uint32_t)pos : 0u);
             });
           },
-          s.rem, sm.dh, &sm.cross, sm.scan, nullptr, nullptr, 1, nbar, nullptr);
+          s.rem, sm.dh, &sm.cross, sm.scan, sm.mm, nullptr, nullptr, nullptr, 1, nbar, nullptr);
     }
     if (t < 4) sm.ctr[t] = 0u;
     __syncthreads();

@@ -61,7 +61,11 @@ struct SlotHeader {
   uint32_t win_cur;    // winner output cursor (rescue)
   uint32_t cand_cur;   // the row's maximum as an order-preserving key (retry)
   uint32_t tie_cur;    // tie tickets (rescue)
-  uint32_t pad[59];    // header is 256 bytes
+  // rescue: per radix level, the digit class's largest key and its smallest
+  // key complemented, merged by atomic max (zero at rest); levels 0..3 of the
+  // selection, then 0..3 of the deterministic tie pick
+  uint32_t class_ext[16];
+  uint32_t pad[43];    // header is 256 bytes
 };
 static_assert(sizeof(SlotHeader) == 256, "slot header size");
 

@@ -261,6 +261,29 @@ __device__ __forceinline__ void wave_minmax(float& mn, float& mx) {
   mx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mx), 63));
 }
 
+// Largest of a and of b over a wave (result in every lane, from lane 63).
+__device__ __forceinline__ void wave_max2_u32(uint32_t& a, uint32_t& b) {
+  const int l = lane_id();
+  const int rl = l & 15;
+  uint32_t x, y;
+#define ERT_STEP(CTRL, COND) \
+  x = dpp_u32<CTRL>(a);      \
+  y = dpp_u32<CTRL>(b);      \
+  if (COND) {                \
+    a = max(a, x);           \
+    b = max(b, y);           \
+  }
+  ERT_STEP(0x111, rl >= 1)
+  ERT_STEP(0x112, rl >= 2)
+  ERT_STEP(0x114, rl >= 4)
+  ERT_STEP(0x118, rl >= 8)
+  ERT_STEP(0x142, (l & 31) >= 16)
+  ERT_STEP(0x143, l >= 32)
+#undef ERT_STEP
+  a = (uint32_t)__builtin_amdgcn_readlane((int)a, 63);
+  b = (uint32_t)__builtin_amdgcn_readlane((int)b, 63);
+}
+
 // Exclusive prefix sum over the block in thread order; `total` gets the sum.
 // `sm` holds BLOCK/64 words.  Contains two __syncthreads.
 // Exclusive offsets of v over the whole workgroup in an arbitrary wave order:
@@ -514,8 +537,10 @@ __device__ __forceinline__ bool finish_slot(SlotHeader* hdr, int G, uint32_t* bc
 // hist_lo up (no round adds below its floor), the digit rows when `dig`, and
 // the header.
 __device__ __forceinline__ void rest_slot(SlotFixed* sf, int t, int block, int hist_lo, bool dig) {
-  if (dig)
+  if (dig) {
     for (int i = t; i < 8 * 256; i += block) (&sf->dig[0][0])[i] = 0u;
+    if (t < 16) sf->hdr.class_ext[t] = 0u;
+  }
   for (int i = hist_lo + t; i < kBins; i += block) sf->hist[i] = 0u;
   if (t == 0) {
     sf->hdr.bar_count = 0u;
@@ -543,34 +568,71 @@ struct RSel {
 // needed.  Afterwards an element is selected iff key >> shift > thr, or
 // key >> shift == thr and it is one of `rem` such elements.  With `gdig`
 // (split rescue) the digit counts of the row's G workgroups are summed
-// through the workspace behind a barrier at each level.
-template <int BLOCK, bool AGG = false, class Iter>
+// through the workspace behind a barrier at each level.  Each level also
+// finds the extremes of the class it counts (the keys that share the digits
+// fixed so far), through `mm` (2 * BLOCK / 64 LDS words) and, split, the
+// eight `gext` words (atomic max, zero at rest): a class holding a single key
+// (all-equal rows, the ties of a two-valued row, a zero class) ends the
+// selection with that key at once instead of after all four levels.  With
+// EXT false (callers short of VGPRs) the extremes are not tracked.
+template <int BLOCK, bool AGG = false, bool EXT = false, class Iter>
 __device__ __forceinline__ RSel radix_select(Iter&& iter, uint32_t need, uint32_t* dh, Cross* cross,
-                                             uint32_t* scan, uint32_t* gdig, SlotHeader* hdr, int G,
+                                             uint32_t* scan, uint32_t* mm, uint32_t* gdig,
+                                             uint32_t* gext, SlotHeader* hdr, int G,
                                              uint32_t& nbar, uint32_t* err) {
+  constexpr int W = BLOCK / 64;
   const int t = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   uint32_t prefix = 0, rem = need, cnt = 0;
   int shift = 24;
   for (int L = 0; L < 4; ++L) {
     shift = 24 - 8 * L;
     for (int i = t; i < 256; i += BLOCK) dh[i] = 0u;
     __syncthreads();
+    uint32_t kmax = 0u, knmin = 0u;  // the class's largest key, smallest complemented
     iter([&](uint32_t key) {
       const bool act = L == 0 || ((key ^ prefix) >> (shift + 8)) == 0u;
       if (AGG)
         lds_inc_agg(dh, (key >> shift) & 255u, act);
       else if (act)
         lds_inc(&dh[(key >> shift) & 255u]);
+      if (EXT && act) {
+        kmax = max(kmax, key);
+        knmin = max(knmin, ~key);
+      }
     });
+    if (EXT) {
+      wave_max2_u32(kmax, knmin);
+      if (lane_id() == 0) {
+        mm[w] = kmax;
+        mm[W + w] = knmin;
+      }
+    }
     __syncthreads();
+    if (EXT) {
+#pragma unroll
+      for (int i = 0; i < W; ++i) {
+        kmax = max(kmax, (uint32_t)__builtin_amdgcn_readfirstlane((int)mm[i]));
+        knmin = max(knmin, (uint32_t)__builtin_amdgcn_readfirstlane((int)mm[W + i]));
+      }
+    }
     if (gdig) {
       uint32_t* gd = gdig + L * 256;
       for (int i = t; i < 256; i += BLOCK) {
         const uint32_t c = dh[i];
         if (c) atomic_add_agent(&gd[i], c);
       }
+      if (EXT && t == 0) {
+        if (kmax) __hip_atomic_fetch_max(&gext[L], kmax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (knmin)
+          __hip_atomic_fetch_max(&gext[4 + L], knmin, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
       row_barrier(hdr, G, nbar, err);
       find_crossing<256, BLOCK>([&](int d) { return load_agent(&gd[d]); }, rem, cross, scan);
+      if (EXT) {
+        kmax = (uint32_t)__builtin_amdgcn_readfirstlane((int)load_agent(&gext[L]));
+        knmin = (uint32_t)__builtin_amdgcn_readfirstlane((int)load_agent(&gext[4 + L]));
+      }
     } else {
       find_crossing<256, BLOCK>([&](int d) { return dh[d]; }, rem, cross, scan);
     }
@@ -579,6 +641,13 @@ __device__ __forceinline__ RSel radix_select(Iter&& iter, uint32_t need, uint32_
     rem -= c.above;
     cnt = c.m;
     if (c.m == rem) break;
+    if (EXT && kmax == ~knmin) {
+      // one key in the class: all of it sits in the crossing digit, and that
+      // key is the threshold
+      prefix = kmax;
+      shift = 0;
+      break;
+    }
   }
   return RSel{prefix >> shift, shift, rem, cnt};
 }
@@ -595,22 +664,23 @@ template <int BLOCK>
 __device__ __forceinline__ void list_select(const uint32_t* key, const int32_t* idx, uint32_t m,
                                             uint32_t need, bool det, int32_t* out, uint32_t base,
                                             uint32_t limit, uint32_t* dh, Cross* cross,
-                                            uint32_t* scan, uint32_t* ctr, uint32_t& nbar) {
+                                            uint32_t* scan, uint32_t* mm, uint32_t* ctr,
+                                            uint32_t& nbar) {
   const int t = threadIdx.x;
   const RSel s = radix_select<BLOCK>(
       [&](auto&& f) {
         for (uint32_t i = t; i < m; i += BLOCK) f(key[i]);
       },
-      need, dh, cross, scan, nullptr, nullptr, 1, nbar, nullptr);
+      need, dh, cross, scan, mm, nullptr, nullptr, nullptr, 1, nbar, nullptr);
   const bool pick = det && s.cnt > s.rem;
   RSel s2{0u, 0, 0u, 0u};
   if (pick) {
-    const uint32_t tk = s.thr;  // the loop ran all four levels: one exact key
+    const uint32_t tk = s.thr;  // the select ended on one exact key
     s2 = radix_select<BLOCK>(
         [&](auto&& f) {
           for (uint32_t i = t; i < m; i += BLOCK) f(key[i] == tk ? ~(uint32_t)idx[i] : 0u);
         },
-        s.rem, dh, cross, scan, nullptr, nullptr, 1, nbar, nullptr);
+        s.rem, dh, cross, scan, mm, nullptr, nullptr, nullptr, 1, nbar, nullptr);
   }
   const uint32_t eq_base = base + (need - s.rem);
   for (uint32_t i = t; i < m; i += BLOCK) {

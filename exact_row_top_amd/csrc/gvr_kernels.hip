@@ -65,6 +65,7 @@ struct alignas(16) Smem {
     } c;
   } u;
   uint32_t dh[256];
+  uint32_t mm[2 * (BLOCK / 64)];  // per-wave class extremes of a radix level
   uint32_t scan[BLOCK / 64];
   float rmin[BLOCK / 64];
   float rmax[BLOCK / 64];
@@ -564,7 +565,7 @@ __global__ void __launch_bounds__(BLOCK)
         rank_select<BLOCK>(sm.u.c.key, sm.u.c.idx, m, need, out, cr.above);
       } else {
         list_select<BLOCK>(sm.u.c.key, sm.u.c.idx, m, need, p.deterministic != 0, out, cr.above,
-                           (uint32_t)K, sm.dh, &sm.cross, sm.scan, sm.ctr, nbar);
+                           (uint32_t)K, sm.dh, &sm.cross, sm.scan, sm.mm, sm.ctr, nbar);
       }
       put_stats(path, (int)cr.m, (int)cr.above, cr.b);
       return;
@@ -928,7 +929,7 @@ __global__ void __launch_bounds__(BLOCK)
           rank_select<BLOCK>(sm.u.c.key, sm.u.c.idx, m, need, out, above);
         } else {
           list_select<BLOCK>(sm.u.c.key, sm.u.c.idx, m, need, p.deterministic != 0, out, above,
-                             (uint32_t)K, sm.dh, &sm.cross, sm.scan, sm.ctr, nbar);
+                             (uint32_t)K, sm.dh, &sm.cross, sm.scan, sm.mm, sm.ctr, nbar);
         }
       }
       // back to zero: the histogram bins the first round added to, and the
@@ -941,8 +942,10 @@ __global__ void __launch_bounds__(BLOCK)
 
   // ---- rescue (a8): exact radix select over the whole row -----------------
   {
-    const RSel s = radix_select<BLOCK, true>(resident, (uint32_t)K, sm.dh, &sm.cross, sm.scan,
-                                             SPLIT ? &sf->dig[0][0] : nullptr, hdr, G, nbar, err);
+    const RSel s = radix_select<BLOCK, true, SPLIT>(resident, (uint32_t)K, sm.dh, &sm.cross, sm.scan,
+                                             sm.mm, SPLIT ? &sf->dig[0][0] : nullptr,
+                                             SPLIT ? &hdr->class_ext[0] : nullptr, hdr, G, nbar,
+                                             err);
     // Deterministic mode: when the K-th key's class holds more scores than
     // are needed, keep its smallest positions -- a second radix select over
     // the class's complemented positions (other scores count as key 0; the
@@ -952,8 +955,8 @@ __global__ void __launch_bounds__(BLOCK)
     const bool pick = p.deterministic && s.cnt > s.rem;
     RSel s2{0u, 0, 0u, 0u};
     if (pick) {
-      const uint32_t tkey = s.thr;  // all four levels ran: one exact key
-      s2 = radix_select<BLOCK, true>(
+      const uint32_t tkey = s.thr;  // the select ended on one exact key
+      s2 = radix_select<BLOCK, true, SPLIT>(
           [&](auto&& f) {
             each([&](int j, int q, bool) {
 #pragma unroll
@@ -965,7 +968,8 @@ __global__ void __launch_bounds__(BLOCK)
               }
             });
           },
-          s.rem, sm.dh, &sm.cross, sm.scan, SPLIT ? &sf->dig[4][0] : nullptr, hdr, G, nbar, err);
+          s.rem, sm.dh, &sm.cross, sm.scan, sm.mm, SPLIT ? &sf->dig[4][0] : nullptr,
+          SPLIT ? &hdr->class_ext[8] : nullptr, hdr, G, nbar, err);
     }
     // a score of the K-th key's class is taken when the tie pick keeps it
     auto kept = [&](int32_t idx) {
