@@ -157,10 +157,10 @@ struct DevInfo {
   bool probed = false;
   bool ok = false;
   int cus = 0;
-  int occ[3][3] = {};      // [k idx][split qpt idx] split-kernel workgroups per CU
-  int occ_api[3][3] = {};  // what hipOccupancyMaxActiveBlocksPerMultiprocessor says
-  int regs[3][3] = {};     // VGPRs per thread of each split kernel
-  int lds[3][3] = {};      // static LDS bytes
+  int occ[3][kNumSplit] = {};      // [k idx][split variant] split-kernel workgroups per CU
+  int occ_api[3][kNumSplit] = {};  // what hipOccupancyMaxActiveBlocksPerMultiprocessor says
+  int regs[3][kNumSplit] = {};     // VGPRs per thread of each split kernel
+  int lds[3][kNumSplit] = {};      // static LDS bytes
   void* slab = nullptr;
   size_t slab_bytes = 0;
 };
@@ -186,7 +186,7 @@ int device_info(DevInfo** out, int* dev_out) {
     d.ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
     d.cus = prop.multiProcessorCount;
     for (int ki = 0; ki < 3; ++ki)
-      for (int qi = 0; qi < 3; ++qi) {
+      for (int qi = 0; qi < kNumSplit; ++qi) {
         const int ks[3] = {512, 1024, 2048};
         const int blk = kSplitVariants[qi].block;
         const void* f = gvr_kernel(ks[ki], blk, kSplitVariants[qi].qpt, true);
@@ -606,9 +606,10 @@ int topk_device_query(int64_t* out) {
   int dev = 0;
   const int rc = device_info(&d, &dev);
   if (rc != TOPK_OK) return rc;
+  static_assert(kNumSplit == 3, "the query's layout holds three split variants");
   out[0] = d->cus;
   for (int ki = 0; ki < 3; ++ki)
-    for (int qi = 0; qi < 3; ++qi) {
+    for (int qi = 0; qi < kNumSplit; ++qi) {
       out[1 + ki * 3 + qi] = d->occ[ki][qi];
       out[10 + ki * 3 + qi] = d->occ_api[ki][qi];
       out[19 + ki * 3 + qi] = d->regs[ki][qi];
