@@ -19,7 +19,8 @@
 //  6. refine: the `need` largest candidates, exactly;
 //  7. rescue when the bracket is invalid or the candidates overflow: an exact
 //     4 x 8-bit radix select over the whole row's resident keys, using every
-//     workgroup of the row, inside the same launch.
+//     workgroup of the row, inside the same launch (it stops early on a digit
+//     class that holds one key).
 //
 // Two tiers share the steps:
 //  * one workgroup per row (SPLIT = false): the whole window is resident in
@@ -31,8 +32,9 @@
 //    surely) is not.  Each counts its part's scores in bins >= b_lo in LDS
 //    and adds those counts into the row's histogram in the workspace; after
 //    one barrier every workgroup reads the merged counts and finds the same
-//    crossing bin, writes its own winners straight to the output (one
-//    cursor per row) and its crossing-bin members to a short list; the last
+//    crossing bin; the suffix counts the workgroups published give each its
+//    offsets.  It appends its crossing-bin members to a short list, counts
+//    itself done, then writes its winners straight to the output; the last
 //    workgroup to finish refines that list.  A row whose merged counts do
 //    not reach K (the floor was too high), whose crossing bin is crowded, or
 //    whose bracket is invalid takes the parallel rescue with all its
