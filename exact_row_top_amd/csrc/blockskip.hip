@@ -383,13 +383,16 @@ __global__ void __launch_bounds__(kBskBlock) topk_blockskip_kernel(const GvrPara
       });
     };
     const uint32_t need = (uint32_t)K - above;
-    const RSel s = radix_select<BLOCK>(iter, need, sm.dh, &sm.cross, sm.scan, sm.mm, nullptr,
-                                       nullptr, nullptr, 1, nbar, nullptr);
+    // (aggregated increments and the single-key stop: tie-heavy rows that
+    // reach this path, e.g. an all-equal row whose maxima all equal the
+    // floor, otherwise pay 64-way LDS conflicts on one digit at every level)
+    const RSel s = radix_select<BLOCK, true, true>(iter, need, sm.dh, &sm.cross, sm.scan, sm.mm,
+                                                   nullptr, nullptr, nullptr, 1, nbar, nullptr);
     const bool pick = p.deterministic && s.cnt > s.rem;
     RSel s2{0u, 0, 0u, 0u};
     if (pick) {
       const uint32_t tk = s.thr;  // the select ended on one exact key
-      s2 = radix_select<BLOCK>(
+      s2 = radix_select<BLOCK, true, true>(
           [&](auto&& f) {
             walk([&](float x, int pos) {
               if (in_class(x)) f(rkey(x) == tk ? ~(uint32_t)pos : 0u);
