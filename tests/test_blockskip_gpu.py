@@ -259,3 +259,26 @@ def test_many_long_rows_take_the_streaming_tier(ert):
     torch.cuda.synchronize()
     assert_parity(w, got.cpu().numpy(), want)
     assert all(st2.cpu().numpy()[r, 6] > 1 for r in long_rows)
+
+
+@pytest.mark.parametrize("dist", ["all_equal", "two_valued", "levels4", "signed_zero"])
+def test_streaming_tier_tie_heavy_rows(ert, dist):
+    """Tie-heavy rows in a batch the plan streams (128 x 65536, K = 512): the
+    maxima give a floor equal to the row's top value class, so the pass ends
+    in its radix ladder; exact, and deterministic ties are the smallest
+    positions."""
+    import torch
+    k, rows, stride = 512, 128, 65536
+    nv = [stride - (r % 5) for r in range(rows)]
+    w = workloads.random_decode(rows, stride, nv, k, seed=len(dist) + 11, dist=dist)
+    want = oracle.topk_workload(w)
+    dev = to_dev(w)
+    log(f"[stream ties] {dist}")
+    st = torch.full((rows, ert.STATS_WORDS), -7, dtype=torch.int32, device="cuda")
+    got = ert.topk_decode(dev["logits"], dev["n_valid"], k, row_stats=st)
+    torch.cuda.synchronize()
+    assert_parity(w, got.cpu().numpy(), want)
+    assert all(st.cpu().numpy()[:, 6] == 1)  # one workgroup per row: the streaming tier
+    got = ert.topk_decode(dev["logits"], dev["n_valid"], k, deterministic=True, sorted=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), want)
