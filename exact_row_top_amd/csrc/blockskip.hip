@@ -210,7 +210,7 @@ __global__ void __launch_bounds__(kBskBlock) topk_blockskip_kernel(const GvrPara
     constexpr int NSB = K / 64;
     float lo = __builtin_inff(), hi = -__builtin_inff();
     for (int j = w; j < NSB; j += W) {
-      const float x = win[(int)(((int64_t)j * (nv - 64)) / (NSB - 1)) + l];
+      const float x = win[SampleStep<NSB>(nv).start(j) + l];
       lo = fminf(lo, x);
       hi = fmaxf(hi, x);
     }

@@ -35,6 +35,37 @@ __device__ __forceinline__ float from_key(uint32_t k) {
 // while the row holds K non-NaN scores.
 __device__ __forceinline__ uint32_t rkey(float x) { return (x == x) ? fkey(x) : 0u; }
 
+// Raw buffer resource, word 3 for gfx9-family parts (32-bit data format,
+// no swizzle); loads past num_records return zeros without a memory access.
+constexpr int kBufWord3 = 0x00020000;
+// Cache policy of streaming loads: non-temporal (the scores are read once).
+constexpr int kCachePolicyNT = 2;
+
+// Raw buffer resource over [p, p + bytes) (p and bytes uniform: both go
+// through readfirstlane so the descriptor lives in scalar registers).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* u = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(u, (short)0, __builtin_amdgcn_readfirstlane(bytes),
+                                           kBufWord3);
+}
+
+// Start of block j of the block64 sample over a window of nv > 64 * NSB scores:
+// floor(j * (nv - 64) / (NSB - 1)).  With nv - 64 = a (NSB - 1) + b, 0 <= b <
+// NSB - 1, that is j a + floor(j b / (NSB - 1)) exactly, so one 32-bit quotient
+// and remainder per row replace a 64-bit division per block (j b < 32 * 32).
+template <int NSB>
+struct SampleStep {
+  uint32_t a, b;
+  __device__ __forceinline__ explicit SampleStep(int nv)
+      : a((uint32_t)(nv - 64) / (uint32_t)(NSB - 1)), b((uint32_t)(nv - 64) % (uint32_t)(NSB - 1)) {}
+  __device__ __forceinline__ int start(int j) const {
+    return (int)((uint32_t)j * a + ((uint32_t)j * b) / (uint32_t)(NSB - 1));
+  }
+};
+
 // A float pinned to a scalar register: as an operand of a VOP3 instruction it
 // takes the one scalar slot instead of a literal the compiler would otherwise
 // rematerialise into a VGPR before every use.

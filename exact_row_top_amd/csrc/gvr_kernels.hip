@@ -187,11 +187,12 @@ __global__ void __launch_bounds__(BLOCK)
   float smp[SPW];
   {
     const float* win = rowp + ks;
+    const SampleStep<NSB> ss(nv);
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
       const int j = w + i * W;
       if (j < NSB) {
-        const int st = (int)(((int64_t)j * (nv - 64)) / (NSB - 1));
+        const int st = ss.start(j);
         smp[i] = win[st + l];
       } else {
         smp[i] = qnan;
@@ -244,32 +245,47 @@ __global__ void __launch_bounds__(BLOCK)
   // part) become NaN markers here: no selection step accepts a NaN (its
   // compares are false, its histogram increment goes to a trash word, its
   // rescue key is the lowest key), and a genuine -inf tie class stays intact.
+  // Per-wave group counts (uniform, computed once): this wave holds groups
+  // j < nj (those starting before the part's end q1), and groups
+  // jf0 <= j < jf1 hold four in-window scores in all 64 lanes ("full": the
+  // passes skip their marker checks).  Every pass compares its unrolled j
+  // with these counts, so no per-group flags stay live across passes.
+  const int qw0 = __builtin_amdgcn_readfirstlane(q0 + w * 64);
+  const int qf1 = min(q1, span >> 2);  // groups wholly inside the window and the part
+  const int nj = __builtin_amdgcn_readfirstlane(qw0 < q1 ? min((q1 - qw0 + BLOCK - 1) / BLOCK, QPT) : 0);
+  const int jf0 = __builtin_amdgcn_readfirstlane((qw0 == 0 && lead > 0) ? 1 : 0);
+  const int jf1 = __builtin_amdgcn_readfirstlane(
+      qw0 + 64 <= qf1 ? min((qf1 - qw0 - 64) / BLOCK + 1, QPT) : 0);
+  // Buffer loads whose range ends at the part's end: lanes past it (only in
+  // the wave holding the part's last group) read zeros without a memory
+  // access and become markers below.  The whole offset sits in the per-lane
+  // offset, which the range check covers.
   f4 v[QPT];
+  {
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(base, q1 * 16);
+    const int vo = (qw0 + l) * 16;
 #pragma unroll
-  for (int j = 0; j < QPT; ++j) {
-    // wave-uniform branches: whole waves inside or outside the part take no
-    // per-lane select
-    const int q = q0 + t + j * BLOCK;
-    if (q < q1) {
-      v[j] = __builtin_nontemporal_load(base + q);
-    } else {
-      v[j] = f4{qnan, qnan, qnan, qnan};
-    }
+    for (int j = 0; j < QPT; ++j)
+      if (j < nj)
+        v[j] = __builtin_bit_cast(
+            f4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, vo + j * BLOCK * 16, 0, kCachePolicyNT));
   }
   // Visit this thread's groups; `full` (uniform per wave) says all 64 lanes
   // hold four in-window scores, so only boundary waves pay for NaN checks.
   auto each = [&](auto&& f) {
-    // An opaque copy of the lane index: every pass recomputes its group
-    // indices instead of the compiler keeping one set live across all passes.
-    int ll = l;
+    // Opaque copies of the lane index and the counts: every pass recomputes
+    // its group indices and tests instead of the compiler keeping one set
+    // live across all passes.
+    int ll = l, njp = nj, jf0p = jf0, jf1p = jf1;
     asm volatile("" : "+v"(ll));
+    asm volatile("" : "+s"(njp));
 #pragma unroll
     for (int j = 0; j < QPT; ++j) {
-      const int qw = q0 + j * BLOCK + w * 64;
-      if (qw >= q1) break;
-      const int q = qw + ll;
-      const bool full = (qw + 64 <= q1) && (qw > 0 || lead == 0) && ((qw + 64) * 4 <= span);
-      f(j, q, full);
+      if (j < njp) {
+        const int q = qw0 + j * BLOCK + ll;
+        const bool full = j >= jf0p && j < jf1p;
+        f(j, q, full);
+      }
     }
   };
   auto resident = [&](auto&& f) {
@@ -362,23 +378,25 @@ __global__ void __launch_bounds__(BLOCK)
       for (int e = 0; e < 3; ++e)
         if (e < lead) v[0][e] = qnan;
     }
-    // last group of the window (tail lanes), if it lies in this part
-    const int qlast = Q - 1;
-    const int tail = span - (qlast << 2);  // valid lanes in the last group, 1..4
-    if (tail < 4 && qlast >= q0 && qlast < q1) {
+    // last group of the part: the lanes after it in its wave hold a copy of
+    // it; in the window's last group the scores past the tail go too
+    if (q1 > q0) {
       // group jl (uniform) of thread tl holds it: only that thread's wave
       // takes the branch, and only group jl's registers are touched
-      const int d = qlast - q0;
+      const int d = q1 - 1 - q0;
       const int jl = d / BLOCK;
       const int tl = d - jl * BLOCK;
-      if (w == (tl >> 6)) {
-        const bool mine = l == (tl & 63);
+      const int lt = tl & 63;
+      const int tail = q1 == Q ? span - ((Q - 1) << 2) : 4;  // scores of the last group, 1..4
+      if (w == (tl >> 6) && (lt < 63 || tail < 4)) {
 #pragma unroll
         for (int j = 0; j < QPT; ++j)
           if (j == jl) {
 #pragma unroll
-            for (int e = 1; e < 4; ++e)
-              if (e >= tail) v[j][e] = mine ? qnan : v[j][e];
+            for (int e = 0; e < 4; ++e) {
+              const bool keep = l < lt || (l == lt && e < tail);
+              v[j][e] = keep ? v[j][e] : qnan;
+            }
           }
       }
     }
