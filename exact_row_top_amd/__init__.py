@@ -41,7 +41,8 @@ class _Options(ctypes.Structure):
                 ("pre_idx_stride", ctypes.c_int64),
                 ("bmax", ctypes.c_void_p),
                 ("bmax_stride", ctypes.c_int64),
-                ("blockskip", ctypes.c_int32)]
+                ("blockskip", ctypes.c_int32),
+                ("barrier_spins", ctypes.c_int32)]
 
 
 TOPK_SORTED = 1
@@ -91,6 +92,8 @@ def load_library():
     lib.topk_workspace_bytes.restype = SZ
     lib.topk_workspace_init.argtypes = [P, SZ, P]
     lib.topk_workspace_init.restype = ctypes.c_int
+    lib.topk_status.argtypes = [P, P]
+    lib.topk_status.restype = ctypes.c_int
     lib.topk_strerror.argtypes = [ctypes.c_int]
     lib.topk_strerror.restype = ctypes.c_char_p
     lib.topk_plan_query.argtypes = [I32, I64, I64, I32, I32, I32, I32, ctypes.POINTER(I64)]
@@ -203,9 +206,10 @@ def _out(indices, rows, k, device):
 
 
 def _opts(force_wgs_per_row, force_rescue, row_stats, rows, values=None, flags=0, hints=None,
-          bmax=None, blockskip=0):
+          bmax=None, blockskip=0, barrier_spins=0):
     import torch
-    if not (force_wgs_per_row or force_rescue or row_stats is not None or blockskip):
+    if not (force_wgs_per_row or force_rescue or row_stats is not None or blockskip
+            or barrier_spins):
         return None
     if row_stats is not None:
         _require(row_stats, "row_stats", torch.int32, 2)
@@ -215,7 +219,8 @@ def _opts(force_wgs_per_row, force_rescue, row_stats, rows, values=None, flags=0
                  row_stats.data_ptr() if row_stats is not None else None,
                  values.data_ptr() if values is not None else None, int(flags),
                  hints[0] if hints else None, hints[1] if hints else 0,
-                 bmax[0] if bmax else None, bmax[1] if bmax else 0, int(blockskip))
+                 bmax[0] if bmax else None, bmax[1] if bmax else 0, int(blockskip),
+                 int(barrier_spins))
     return ctypes.pointer(o)
 
 
@@ -287,7 +292,8 @@ def _ws(workspace):
 def topk_decode(logits, n_valid, k: int, indices=None, *, workspace=None, stream=None,
                 values=None, return_values: bool = False, sorted: bool = False,
                 deterministic: bool = False, pre_idx=None, bmax=None, blockskip: int = 0,
-                force_wgs_per_row: int = 0, force_rescue: bool = False, row_stats=None):
+                force_wgs_per_row: int = 0, force_rescue: bool = False, row_stats=None,
+                barrier_spins: int = 0):
     """Exact top-k of logits[r, :n_valid[r]] per row (local indices, -1 pad).
 
     values / return_values: also the selected scores (-FLT_MAX pad); sorted:
@@ -311,7 +317,7 @@ def topk_decode(logits, n_valid, k: int, indices=None, *, workspace=None, stream
     bm = _bmax(bmax, rows, row_stride, logits.device)
     wp, wb = _ws(workspace)
     opts = _opts(force_wgs_per_row, force_rescue, row_stats, rows, vals, flags, hints, bm,
-                 blockskip)
+                 blockskip, barrier_spins)
     s = _stream_ptr(stream, logits.device)
     if opts is not None:
         rc = lib.topk_decode_ex(logits.data_ptr(), row_stride, n_valid.data_ptr(), rows, k,
@@ -345,7 +351,7 @@ def topk_decode(logits, n_valid, k: int, indices=None, *, workspace=None, stream
 def topk_prefill(logits, row_starts, row_ends, k: int, indices=None, *, max_row_len: int = 0,
                  workspace=None, stream=None, values=None, return_values: bool = False,
                  sorted: bool = False, deterministic: bool = False, force_wgs_per_row: int = 0,
-                 force_rescue: bool = False, row_stats=None):
+                 force_rescue: bool = False, row_stats=None, barrier_spins: int = 0):
     """Exact top-k of logits[r, row_starts[r]:row_ends[r]] per row (ks-relative).
 
     Output options as for topk_decode."""
@@ -360,7 +366,8 @@ def topk_prefill(logits, row_starts, row_ends, k: int, indices=None, *, max_row_
     vals = _values(values, return_values, rows, k, logits.device)
     flags = _flags(sorted, deterministic)
     wp, wb = _ws(workspace)
-    opts = _opts(force_wgs_per_row, force_rescue, row_stats, rows, vals, flags)
+    opts = _opts(force_wgs_per_row, force_rescue, row_stats, rows, vals, flags,
+                 barrier_spins=barrier_spins)
     s = _stream_ptr(stream, logits.device)
     if opts is not None:
         rc = lib.topk_prefill_ex(logits.data_ptr(), row_stride, row_starts.data_ptr(),
@@ -383,7 +390,8 @@ def topk_decode_varlen(logits, kv_lens, k: int, next_n: int = 1, compress_ratio:
                        indices=None, *, workspace=None, stream=None, values=None,
                        return_values: bool = False, sorted: bool = False,
                        deterministic: bool = False, pre_idx=None, bmax=None, blockskip: int = 0,
-                       force_wgs_per_row: int = 0, force_rescue: bool = False, row_stats=None):
+                       force_wgs_per_row: int = 0, force_rescue: bool = False, row_stats=None,
+                       barrier_spins: int = 0):
     """Exact top-k of the varlen / MTP decode form: row r selects from
     logits[r, :n] with n = (kv_lens[r // next_n] - next_n + r % next_n + 1) //
     compress_ratio (no window when kv_lens[r // next_n] < next_n), computed on
@@ -404,7 +412,7 @@ def topk_decode_varlen(logits, kv_lens, k: int, next_n: int = 1, compress_ratio:
     bm = _bmax(bmax, rows, row_stride, logits.device)
     wp, wb = _ws(workspace)
     opts = _opts(force_wgs_per_row, force_rescue, row_stats, rows, vals, flags, hints, bm,
-                 blockskip)
+                 blockskip, barrier_spins)
     if opts is None and bm is not None:
         opts = ctypes.pointer(_Options(0, 0, None, vals.data_ptr() if vals is not None else None,
                                        int(flags), hints[0] if hints else None,
@@ -429,6 +437,18 @@ def topk_decode_varlen(logits, kv_lens, k: int, next_n: int = 1, compress_ratio:
     return (out, vals) if vals is not None else out
 
 
+def status(device="cuda", stream=None):
+    """Stream-ordered count of split-tier row-barrier waits that gave up since
+    the previous status() on this device (their calls' results are undefined),
+    as an int32 [1] device tensor; the count is reset.  A non-zero count also
+    re-zeroes the library-owned slab (caller workspaces need
+    topk_workspace_init)."""
+    import torch
+    out = torch.zeros(1, dtype=torch.int32, device=device)
+    _check(load_library().topk_status(out.data_ptr(), _stream_ptr(stream, out.device)))
+    return out
+
+
 def new_workspace(num_rows: int, row_stride: int, k: int, device="cuda", stream=None):
     """Allocate and zero a caller-owned workspace (None when the plan needs none)."""
     import torch
@@ -440,6 +460,7 @@ def new_workspace(num_rows: int, row_stride: int, k: int, device="cuda", stream=
     return ws
 
 
-__all__ = ["topk_decode", "topk_prefill", "topk_decode_varlen", "block_max", "workspace_bytes", "new_workspace", "plan_query",
+__all__ = ["topk_decode", "topk_prefill", "topk_decode_varlen", "block_max", "workspace_bytes",
+           "new_workspace", "status", "plan_query",
            "strerror", "load_library", "TopKError", "STATS_WORDS", "VALID_K", "TOPK_SORTED",
            "TOPK_DETERMINISTIC"]

@@ -387,7 +387,7 @@ __global__ void __launch_bounds__(kBskBlock) topk_blockskip_kernel(const GvrPara
     // reach this path, e.g. an all-equal row whose maxima all equal the
     // floor, otherwise pay 64-way LDS conflicts on one digit at every level)
     const RSel s = radix_select<BLOCK, true, true>(iter, need, sm.dh, &sm.cross, sm.scan, sm.mm,
-                                                   nullptr, nullptr, nullptr, 1, nbar, nullptr);
+                                                   nullptr, nullptr, nullptr, 1, nbar, BarrierSync{});
     const bool pick = p.deterministic && s.cnt > s.rem;
     RSel s2{0u, 0, 0u, 0u};
     if (pick) {
@@ -398,7 +398,7 @@ __global__ void __launch_bounds__(kBskBlock) topk_blockskip_kernel(const GvrPara
               if (in_class(x)) f(rkey(x) == tk ? ~(uint32_t)pos : 0u);
             });
           },
-          s.rem, sm.dh, &sm.cross, sm.scan, sm.mm, nullptr, nullptr, nullptr, 1, nbar, nullptr);
+          s.rem, sm.dh, &sm.cross, sm.scan, sm.mm, nullptr, nullptr, nullptr, 1, nbar, BarrierSync{});
     }
     if (t < 4) sm.ctr[t] = 0u;
     __syncthreads();

@@ -45,7 +45,7 @@ constexpr int kStatsWords = 9;
 constexpr int kBskMaxBlocks = 8192;  // rows the streaming pass takes: <= this many blocks of 32
 
 // Workspace layout (bytes):
-//   [0, 256)                             error flags (word 0)
+//   [0, 256)                             header (unused)
 //   kMaxSlots fixed blocks of 17664 bytes: SlotHeader, digit counts [8][256],
 //   value histogram [kBins]
 //   then one data block per slot: G slices of kBins suffix counts (slice g:
@@ -92,8 +92,13 @@ constexpr size_t ws_bytes_for(int slots, int G) {
   return kWsDataOff + (size_t)slots * slot_data_bytes(G);
 }
 
-// Error flags written by the kernel into workspace word 0.
-constexpr uint32_t kErrBarrierTimeout = 1u;
+// The split tier's bounded row-barrier waits: the per-device count a wait
+// that gives up adds to, and the polls a wait makes first.
+struct BarrierSync {
+  uint32_t* err = nullptr;
+  uint32_t spins = 0;
+};
+constexpr uint32_t kDefaultSpins = 1u << 24;
 
 // Varlen / MTP decode form (the heuristic decode contract of PR 18122,
 // run_varlen commit): row r belongs to request r / next_n, whose total cache
@@ -126,6 +131,7 @@ struct GvrParams {
   int32_t* indices;
   int32_t* row_stats;  // optional
   unsigned char* ws;   // workspace base (split tier), or nullptr
+  BarrierSync sync;    // split tier: timeout count and poll limit
 };
 
 // Output epilogue (values, sorting): one workgroup per row.

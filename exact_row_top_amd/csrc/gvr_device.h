@@ -532,9 +532,11 @@ __device__ __forceinline__ float bin_edge(int b, const BinMap& bm) {
 // crosses between workgroups is an agent-scope atomic (adds, loads, stores),
 // so no cache write-back or invalidate is needed: each wave only waits for
 // its own atomics to complete before the workgroup arrives.  Spins are
-// bounded: on timeout an error flag is raised in the workspace and the
-// workgroup moves on (results are then undefined, but every wave exits).
-__device__ __forceinline__ void row_barrier(SlotHeader* hdr, int G, uint32_t& nbar, uint32_t* err) {
+// bounded (sy.spins polls): a wait that gives up adds one to the library's
+// per-device timeout count (read by topk_status) and the workgroup moves on
+// (that call's results are then undefined, but every wave exits).
+__device__ __forceinline__ void row_barrier(SlotHeader* hdr, int G, uint32_t& nbar,
+                                            const BarrierSync& sy) {
   wait_vm();
   __syncthreads();
   ++nbar;
@@ -544,8 +546,8 @@ __device__ __forceinline__ void row_barrier(SlotHeader* hdr, int G, uint32_t& nb
     uint32_t spins = 0;
     while (load_agent(&hdr->bar_count) < target) {
       __builtin_amdgcn_s_sleep(1);
-      if (++spins > (1u << 24)) {
-        atomic_add_agent_nr(err, kErrBarrierTimeout);
+      if (++spins > sy.spins) {
+        atomic_add_agent_nr(sy.err, 1u);
         break;
       }
     }
@@ -610,7 +612,7 @@ template <int BLOCK, bool AGG = false, bool EXT = false, class Iter>
 __device__ __forceinline__ RSel radix_select(Iter&& iter, uint32_t need, uint32_t* dh, Cross* cross,
                                              uint32_t* scan, uint32_t* mm, uint32_t* gdig,
                                              uint32_t* gext, SlotHeader* hdr, int G,
-                                             uint32_t& nbar, uint32_t* err) {
+                                             uint32_t& nbar, const BarrierSync& sy) {
   constexpr int W = BLOCK / 64;
   const int t = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -658,7 +660,7 @@ __device__ __forceinline__ RSel radix_select(Iter&& iter, uint32_t need, uint32_
         if (knmin)
           __hip_atomic_fetch_max(&gext[4 + L], knmin, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      row_barrier(hdr, G, nbar, err);
+      row_barrier(hdr, G, nbar, sy);
       find_crossing<256, BLOCK>([&](int d) { return load_agent(&gd[d]); }, rem, cross, scan);
       if (EXT) {
         kmax = (uint32_t)__builtin_amdgcn_readfirstlane((int)load_agent(&gext[L]));
@@ -702,7 +704,7 @@ __device__ __forceinline__ void list_select(const uint32_t* key, const int32_t* 
       [&](auto&& f) {
         for (uint32_t i = t; i < m; i += BLOCK) f(key[i]);
       },
-      need, dh, cross, scan, mm, nullptr, nullptr, nullptr, 1, nbar, nullptr);
+      need, dh, cross, scan, mm, nullptr, nullptr, nullptr, 1, nbar, BarrierSync{});
   const bool pick = det && s.cnt > s.rem;
   RSel s2{0u, 0, 0u, 0u};
   if (pick) {
@@ -711,7 +713,7 @@ __device__ __forceinline__ void list_select(const uint32_t* key, const int32_t* 
         [&](auto&& f) {
           for (uint32_t i = t; i < m; i += BLOCK) f(key[i] == tk ? ~(uint32_t)idx[i] : 0u);
         },
-        s.rem, dh, cross, scan, mm, nullptr, nullptr, nullptr, 1, nbar, nullptr);
+        s.rem, dh, cross, scan, mm, nullptr, nullptr, nullptr, 1, nbar, BarrierSync{});
   }
   const uint32_t eq_base = base + (need - s.rem);
   for (uint32_t i = t; i < m; i += BLOCK) {

@@ -165,14 +165,12 @@ __global__ void __launch_bounds__(BLOCK)
   SlotHeader* hdr = nullptr;
   uint32_t* slices = nullptr;  // per-workgroup suffix counts [G][kBins]
   uint2* s_pair = nullptr;     // crossing-bin members (key, index)
-  uint32_t* err = nullptr;
   if (SPLIT) {
     sf = reinterpret_cast<SlotFixed*>(p.ws + kWsHeaderBytes) + slot;
     hdr = &sf->hdr;
     unsigned char* data = p.ws + kWsDataOff + (size_t)slot * slot_data_bytes(G);
     slices = reinterpret_cast<uint32_t*>(data);
     s_pair = reinterpret_cast<uint2*>(data + (size_t)G * kSliceBytes);
-    err = reinterpret_cast<uint32_t*>(p.ws);
   }
 
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave index, uniform
@@ -731,7 +729,7 @@ __global__ void __launch_bounds__(BLOCK)
           }
         }
       }
-      row_barrier(hdr, G, nbar, err);
+      row_barrier(hdr, G, nbar, p.sync);
       {
         constexpr int BPT = kBins / BLOCK;
         uint32_t r[BPT];
@@ -786,7 +784,7 @@ __global__ void __launch_bounds__(BLOCK)
                                    __HIP_MEMORY_SCOPE_AGENT);
         }
         const float lo = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sm.thr[0])));
-        row_barrier(hdr, G, nbar, err);
+        row_barrier(hdr, G, nbar, p.sync);
         const uint32_t tk = __builtin_amdgcn_readfirstlane(load_agent(&hdr->cand_cur));
         const float top = tk ? from_key(tk) : -__builtin_inff();
         const float sc = (float)kBins / (top - lo);
@@ -815,10 +813,10 @@ __global__ void __launch_bounds__(BLOCK)
         } else {
           // the rescue merges its digit counts in those rows: every
           // workgroup has read them; back to zero, then on
-          row_barrier(hdr, G, nbar, err);
+          row_barrier(hdr, G, nbar, p.sync);
           for (int i = t; i < 8 * 256; i += BLOCK)
             __hip_atomic_store(&sf->dig[0][0] + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          row_barrier(hdr, G, nbar, err);
+          row_barrier(hdr, G, nbar, p.sync);
         }
       }
     }
@@ -965,7 +963,7 @@ __global__ void __launch_bounds__(BLOCK)
     const RSel s = radix_select<BLOCK, true, SPLIT>(resident, (uint32_t)K, sm.dh, &sm.cross, sm.scan,
                                              sm.mm, SPLIT ? &sf->dig[0][0] : nullptr,
                                              SPLIT ? &hdr->class_ext[0] : nullptr, hdr, G, nbar,
-                                             err);
+                                             p.sync);
     // Deterministic mode: when the K-th key's class holds more scores than
     // are needed, keep its smallest positions -- a second radix select over
     // the class's complemented positions (other scores count as key 0; the
@@ -989,7 +987,7 @@ __global__ void __launch_bounds__(BLOCK)
             });
           },
           s.rem, sm.dh, &sm.cross, sm.scan, sm.mm, SPLIT ? &sf->dig[4][0] : nullptr,
-          SPLIT ? &hdr->class_ext[8] : nullptr, hdr, G, nbar, err);
+          SPLIT ? &hdr->class_ext[8] : nullptr, hdr, G, nbar, p.sync);
     }
     // a score of the K-th key's class is taken when the tie pick keeps it
     auto kept = [&](int32_t idx) {

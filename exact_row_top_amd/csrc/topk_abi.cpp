@@ -16,6 +16,9 @@ const void* gvr_kernel(int k, int block, int qpt, bool split);
 const void* epilogue_kernel(int k);
 const void* blockskip_kernel(int k, bool self);
 const void* block_max_kernel_ptr();
+hipError_t state_timeout_address(uint32_t** out);
+const void* status_read_kernel_ptr();
+const void* status_reset_kernel_ptr();
 }
 
 using namespace ert;
@@ -163,6 +166,7 @@ struct DevInfo {
   int lds[3][kNumSplit] = {};      // static LDS bytes
   void* slab = nullptr;
   size_t slab_bytes = 0;
+  uint32_t* timeout = nullptr;  // this GPU's row-barrier timeout count
 };
 constexpr int kMaxDev = 64;
 DevInfo g_dev[kMaxDev];
@@ -185,6 +189,7 @@ int device_info(DevInfo** out, int* dev_out) {
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return TOPK_EDEVICE;
     d.ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
     d.cus = prop.multiProcessorCount;
+    if (d.ok && state_timeout_address(&d.timeout) != hipSuccess) d.ok = false;
     for (int ki = 0; ki < 3; ++ki)
       for (int qi = 0; qi < kNumSplit; ++qi) {
         const int ks[3] = {512, 1024, 2048};
@@ -296,6 +301,7 @@ int run(int mode, const float* logits, int64_t row_stride, const int32_t* e1, co
   const float* bmax = opts ? opts->bmax : nullptr;
   const int32_t bsk_mode = opts ? opts->blockskip : 0;
   if (bsk_mode < -1 || bsk_mode > 2) return TOPK_EINVAL;
+  if (opts && opts->barrier_spins < 0) return TOPK_EINVAL;
   if (bsk_mode == 2 && (mode != 0 || (row_stride + 31) / 32 > kBskMaxBlocks)) return TOPK_EINVAL;
   if (bmax) {
     if (mode != 0) return TOPK_EINVAL;  // block-skip serves the decode forms
@@ -328,6 +334,8 @@ int run(int mode, const float* logits, int64_t row_stride, const int32_t* e1, co
   prm.deterministic = (flags & TOPK_DETERMINISTIC) ? 1 : 0;
   prm.indices = indices;
   prm.row_stats = opts ? opts->row_stats : nullptr;
+  prm.sync.err = d->timeout;
+  prm.sync.spins = (opts && opts->barrier_spins > 0) ? (uint32_t)opts->barrier_spins : kDefaultSpins;
 
   const bool given = bmax && bsk_mode >= 0 &&
                      (bsk_mode == 1 || blockskip_gate(num_rows, row_stride, k));
@@ -375,9 +383,15 @@ int run(int mode, const float* logits, int64_t row_stride, const int32_t* e1, co
           d->slab = nullptr;
           d->slab_bytes = 0;
         }
+        // zeroed before any stream can use it: the memset completes before
+        // the call returns (allocation is not capture-safe either way)
         void* ptr = nullptr;
         if (hipMalloc(&ptr, want) != hipSuccess) return TOPK_ELAUNCH;
-        if (hipMemsetAsync(ptr, 0, want, stream) != hipSuccess) return TOPK_ELAUNCH;
+        if (hipMemsetAsync(ptr, 0, want, stream) != hipSuccess ||
+            hipStreamSynchronize(stream) != hipSuccess) {
+          (void)hipFree(ptr);
+          return TOPK_ELAUNCH;
+        }
         d->slab = ptr;
         d->slab_bytes = want;
       }
@@ -566,6 +580,27 @@ int topk_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t str
   if (!workspace_bytes) return TOPK_OK;
   return hipMemsetAsync(workspace, 0, workspace_bytes, stream) == hipSuccess ? TOPK_OK
                                                                               : TOPK_ELAUNCH;
+}
+
+int topk_status(int32_t* timeouts, hipStream_t stream) {
+  if (!timeouts) return TOPK_EINVAL;
+  if (!aligned(timeouts, 4)) return TOPK_ELAYOUT;
+  std::lock_guard<std::mutex> lock(g_mu);
+  DevInfo* d = nullptr;
+  int dev = 0;
+  const int rc = device_info(&d, &dev);
+  if (rc != TOPK_OK) return rc;
+  uint4* slab = static_cast<uint4*>(d->slab);
+  size_t n0 = d->slab_bytes / 16;
+  uint4* none = nullptr;
+  size_t n1 = 0;
+  void* a1[] = {&d->timeout, &timeouts, &slab, &n0, &none, &n1};
+  if (hipLaunchKernel(status_read_kernel_ptr(), dim3(256), dim3(256), a1, 0, stream) != hipSuccess)
+    return TOPK_ELAUNCH;
+  void* a2[] = {&d->timeout};
+  if (hipLaunchKernel(status_reset_kernel_ptr(), dim3(1), dim3(64), a2, 0, stream) != hipSuccess)
+    return TOPK_ELAUNCH;
+  return hipGetLastError() == hipSuccess ? TOPK_OK : TOPK_ELAUNCH;
 }
 
 const char* topk_strerror(int status) {

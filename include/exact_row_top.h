@@ -38,22 +38,31 @@
  *  - indices: int32 [num_rows][k], 4-byte aligned.  Long rows (nv > k) get k
  *    distinct positions in [0, nv) in unspecified order; short rows get
  *    0..nv-1 then -1.
- *  - NaN inside a window is outside the contract (PR 18122, varlen commit:
- *    "NaN-ordering limitation"): the kernel stays memory-safe and still writes
- *    k distinct in-window indices, but which ones is unspecified.  +-inf are
- *    ordinary values; -0 and +0 are equal.
+ *  - NaN inside a window is outside the contract (PR 18122, the commit that
+ *    documents run_varlen's inherited NaN-ordering limitation): the kernels
+ *    stay memory-safe on such a row (every read and write stays inside the
+ *    row's stride, its k output slots and the workspace), but the k indices
+ *    written for it are unspecified: they need not be distinct, nor inside
+ *    the window.  +-inf are ordinary values; -0 and +0 are equal.
  *  - workspace: optional caller-owned device buffer of at least
  *    topk_workspace_bytes(...) bytes, zeroed ONCE by topk_workspace_init before
  *    its first use; every call returns it to that resting state (histograms,
- *    cursors and counters back to zero; only a per-row barrier generation word
- *    keeps counting), so a captured graph can replay without a memset.  The
+ *    cursors and counters back to zero), so a captured graph can replay
+ *    without a memset.  The
  *    split tier's row barriers need the workgroups of a launch to be resident
  *    together; the plan bounds each launch by the device's resident capacity,
  *    so kernels that pin the GPU's compute units for their whole lifetime must
- *    not run beside these calls.  Calls that run concurrently (different
- *    streams) must not share one workspace.  NULL selects a per-device slab
- *    the library allocates on first need, keeps until process exit, and grows
- *    only when a larger plan needs it (allocation is not capture-safe).
+ *    not run beside these calls; a row barrier that waits too long gives up,
+ *    the call's results are then undefined, and topk_status reports it.
+ *    Calls that run concurrently (different streams) must not share one
+ *    workspace (PR 18122, "varlen engine and seam" commit: a caller
+ *    workspace so that concurrent streams do not share the split tier's
+ *    publish slab).  NULL selects a per-device slab (PR 18122, first commit:
+ *    per-device workspace slab) the library allocates on first need, zeroes
+ *    before the call returns, keeps until process exit, and grows only when a
+ *    larger plan needs it (allocation is not capture-safe).  There is one slab
+ *    per GPU: calls with a NULL workspace must all go to one stream, or be
+ *    ordered across streams by the caller.
  *  - Return value: TOPK_OK or one of the TOPK_E* codes below; nothing else
  *    crosses the ABI (no exceptions).  Argument errors are detected on the
  *    host before anything is launched.
@@ -202,16 +211,42 @@ int topk_decode_blockskip(const float* logits, int64_t row_stride, const int32_t
 int topk_block_max(const float* logits, int64_t row_stride, int32_t num_rows, float* bmax,
                    int64_t bmax_stride, hipStream_t stream);
 
+/* ---- Caller workspace and status ----------------------------------------
+ * The pages' runner takes an optional caller workspace (PR 18122: run_ws
+ * with a caller workspace, first commit; run_varlen(workspace=...) in the
+ * "varlen engine and seam" commit, so that concurrent streams do not share
+ * one publish slab).  These calls size, prepare and audit one. */
+
 /* Bytes of workspace a call with num_rows rows of stride `max_row_len` needs
  * (pass the row_stride of the call; 0 when the plan uses one workgroup per
  * row and needs none).  The value does not depend on the device.  Returns 0
- * for invalid arguments as well. */
+ * for invalid arguments as well.  Host only: no device access. */
 size_t topk_workspace_bytes(int32_t num_rows, int64_t max_row_len, int32_t k);
 
-/* Zero a workspace once before its first use (stream-ordered memset). */
+/* Zero a workspace once before its first use: a stream-ordered memset of
+ * workspace_bytes bytes of the caller's device buffer (the library keeps no
+ * reference to it).  workspace NULL with workspace_bytes 0 is a no-op;
+ * NULL with a size gives TOPK_EINVAL; a failed memset TOPK_ELAUNCH.  Not for
+ * use inside a captured graph (it records a memset node); a zeroed workspace
+ * stays zeroed between calls, so a graph needs none. */
 int topk_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Static text for a status code. */
+/* Stream-ordered audit of the split tier's bounded waits on the current
+ * device.  Writes to *timeouts (device int32, 4-byte aligned) the number of
+ * row-barrier waits that gave up since the previous topk_status on this
+ * device, then resets that count.  A non-zero count means some call since
+ * then returned undefined indices (its workgroups were not all resident
+ * together: another kernel held compute units).  When the count is non-zero
+ * the same launch also re-zeroes the library-owned slab; any caller
+ * workspace used since then must be re-zeroed with topk_workspace_init
+ * before its next use.  Two kernels on `stream`, no allocation, no host
+ * sync; timeouts NULL gives TOPK_EINVAL. */
+int topk_status(int32_t* timeouts, hipStream_t stream);
+
+/* Static text for a status code (the pages' calls raise contract errors
+ * loudly instead of falling back: PR 18122, the run_varlen production commit
+ * and its fp32-contract commit).  Never NULL; unknown codes give
+ * "unknown status". */
 const char* topk_strerror(int status);
 
 /* ---- Test and diagnostic surface ------------------------------------------
@@ -259,6 +294,12 @@ typedef struct topk_options {
                              maxima it makes itself in a first streaming pass
                              (decode forms, rows of at most 8192 blocks of
                              32; bmax unused) */
+  int32_t barrier_spins;  /* polls a split-tier row-barrier wait makes before
+                             it gives up: 0 = the default (2^24, about a
+                             second), n > 0 = n; < 0 gives TOPK_EINVAL.
+                             Small values make waits give up on purpose
+                             (undefined results, counted by topk_status):
+                             for tests of that path only. */
 } topk_options;
 
 int topk_decode_ex(const float* logits, int64_t row_stride, const int32_t* n_valid,

@@ -208,3 +208,17 @@ def test_output_options_and_varlen_validation():
     assert lib.topk_decode_varlen_hinted(None, 4096, None, None, 0, 0, 2, 4, 512, None, None, 0,
                                          None, 0, None) == 0
     assert _validate(stride=1 << 30) == ert.TOPK_EINVAL
+
+
+def test_status_rejects_bad_output_without_a_device():
+    lib = ert.load_library()
+    assert lib.topk_status(None, None) == ert.TOPK_EINVAL
+    assert lib.topk_status(P16 + 2, None) == ert.TOPK_ELAYOUT
+
+
+def test_options_reject_negative_barrier_spins():
+    # validated on the host before any device query
+    o = ert._Options(0, 0, None, None, 0, None, 0, None, 0, 0, -1)
+    lib = ert.load_library()
+    rc = lib.topk_decode_ex(P16, 4096, P16, 4, 512, P16, None, 0, None, ctypes.pointer(o))
+    assert rc == ert.TOPK_EINVAL
