@@ -92,6 +92,8 @@ def load_library():
     lib.topk_workspace_bytes.restype = SZ
     lib.topk_workspace_init.argtypes = [P, SZ, P]
     lib.topk_workspace_init.restype = ctypes.c_int
+    lib.topk_decode_noalloc.argtypes = [P, I64, P, I32, I32, P, P]
+    lib.topk_decode_noalloc.restype = ctypes.c_int
     lib.topk_status.argtypes = [P, P]
     lib.topk_status.restype = ctypes.c_int
     lib.topk_strerror.argtypes = [ctypes.c_int]

@@ -100,6 +100,11 @@ struct BarrierSync {
 };
 constexpr uint32_t kDefaultSpins = 1u << 24;
 
+// Fixed split-tier workspace of the entry point that allocates nothing: it
+// holds every decode plan on a 256-compute-unit device (the largest needs
+// about 22 MB); plans needing more are rejected.
+constexpr size_t kScratchBytes = (size_t)24 << 20;
+
 // Varlen / MTP decode form (the heuristic decode contract of PR 18122,
 // run_varlen commit): row r belongs to request r / next_n, whose total cache
 // length is kv_lens[r / next_n]; its window is [0, n) with

@@ -17,6 +17,8 @@ const void* epilogue_kernel(int k);
 const void* blockskip_kernel(int k, bool self);
 const void* block_max_kernel_ptr();
 hipError_t state_timeout_address(uint32_t** out);
+hipError_t state_scratch_address(void** out);
+const void* fill_zero_kernel_ptr();
 const void* status_read_kernel_ptr();
 const void* status_reset_kernel_ptr();
 }
@@ -167,6 +169,8 @@ struct DevInfo {
   void* slab = nullptr;
   size_t slab_bytes = 0;
   uint32_t* timeout = nullptr;  // this GPU's row-barrier timeout count
+  void* scratch = nullptr;      // this GPU's fixed workspace (topk_decode_noalloc)
+  bool scratch_cleared = false;
 };
 constexpr int kMaxDev = 64;
 DevInfo g_dev[kMaxDev];
@@ -189,7 +193,11 @@ int device_info(DevInfo** out, int* dev_out) {
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return TOPK_EDEVICE;
     d.ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
     d.cus = prop.multiProcessorCount;
-    if (d.ok && state_timeout_address(&d.timeout) != hipSuccess) d.ok = false;
+    // set-up, with this device current: its copies of the library's device
+    // variables (the host-side names are stand-ins, never device addresses)
+    if (d.ok && (state_timeout_address(&d.timeout) != hipSuccess || !d.timeout ||
+                 state_scratch_address(&d.scratch) != hipSuccess || !d.scratch))
+      d.ok = false;
     for (int ki = 0; ki < 3; ++ki)
       for (int qi = 0; qi < kNumSplit; ++qi) {
         const int ks[3] = {512, 1024, 2048};
@@ -282,7 +290,7 @@ int launch_epilogue(const GvrParams& prm, int32_t k, int32_t num_rows, float* va
 int run(int mode, const float* logits, int64_t row_stride, const int32_t* e1, const int32_t* e2,
         int32_t num_rows, int32_t k, int32_t* indices, int64_t max_row_len, void* workspace,
         size_t workspace_bytes, hipStream_t stream, const topk_options* opts,
-        const VarlenForm* vf = nullptr) {
+        const VarlenForm* vf = nullptr, bool use_scratch = false) {
   const int32_t force_g = opts ? opts->force_wgs_per_row : 0;
   int rc = validate(mode, logits, row_stride, e1, e2, num_rows, k, indices, force_g);
   if (rc != TOPK_OK) return rc;
@@ -321,6 +329,22 @@ int run(int mode, const float* logits, int64_t row_stride, const int32_t* e1, co
   int dev = 0;
   rc = device_info(&d, &dev);
   if (rc != TOPK_OK) return rc;
+
+  if (use_scratch) {
+    // the fixed per-device scratch stands in for the workspace: nothing is
+    // allocated; its first use on this device clears it with a kernel on the
+    // caller's stream (the array rests at zero between calls after that)
+    workspace = d->scratch;
+    workspace_bytes = kScratchBytes;
+    if (!d->scratch_cleared) {
+      uint4* p = static_cast<uint4*>(d->scratch);
+      size_t n = kScratchBytes / 16;
+      void* a[] = {&p, &n};
+      if (hipLaunchKernel(fill_zero_kernel_ptr(), dim3(256), dim3(256), a, 0, stream) != hipSuccess)
+        return TOPK_ELAUNCH;
+      d->scratch_cleared = true;
+    }
+  }
 
   GvrParams prm;
   memset(&prm, 0, sizeof(prm));
@@ -442,6 +466,12 @@ int topk_prefill(const float* logits, int64_t row_stride, const int32_t* row_sta
                  int64_t max_row_len, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return run(1, logits, row_stride, row_starts, row_ends, num_rows, k, indices, max_row_len,
              workspace, workspace_bytes, stream, nullptr);
+}
+
+int topk_decode_noalloc(const float* logits, int64_t row_stride, const int32_t* n_valid,
+                        int32_t num_rows, int32_t k, int32_t* indices, hipStream_t stream) {
+  return run(0, logits, row_stride, n_valid, nullptr, num_rows, k, indices, 0, nullptr, 0, stream,
+             nullptr, nullptr, true);
 }
 
 int topk_decode_v(const float* logits, int64_t row_stride, const int32_t* n_valid,
@@ -592,9 +622,9 @@ int topk_status(int32_t* timeouts, hipStream_t stream) {
   if (rc != TOPK_OK) return rc;
   uint4* slab = static_cast<uint4*>(d->slab);
   size_t n0 = d->slab_bytes / 16;
-  uint4* none = nullptr;
-  size_t n1 = 0;
-  void* a1[] = {&d->timeout, &timeouts, &slab, &n0, &none, &n1};
+  uint4* scr = static_cast<uint4*>(d->scratch);
+  size_t n1 = d->scratch_cleared ? kScratchBytes / 16 : 0;
+  void* a1[] = {&d->timeout, &timeouts, &slab, &n0, &scr, &n1};
   if (hipLaunchKernel(status_read_kernel_ptr(), dim3(256), dim3(256), a1, 0, stream) != hipSuccess)
     return TOPK_ELAUNCH;
   void* a2[] = {&d->timeout};

@@ -89,7 +89,9 @@ enum {
                           the window's start) */
   TOPK_ELAYOUT = 2,    /* logits not 16-byte aligned, row_stride % 4 != 0,
                           indices / extents not 4-byte aligned */
-  TOPK_EWORKSPACE = 3, /* caller workspace smaller than topk_workspace_bytes */
+  TOPK_EWORKSPACE = 3, /* caller workspace smaller than topk_workspace_bytes
+                          (topk_decode_noalloc: a plan larger than its fixed
+                          scratch) */
   TOPK_EDEVICE = 4,    /* current device is not gfx950, or no device */
   TOPK_ELAUNCH = 5,    /* a HIP launch or allocation failed */
 };
@@ -111,6 +113,22 @@ int topk_prefill(const float* logits, int64_t row_stride, const int32_t* row_sta
                  const int32_t* row_ends, int32_t num_rows, int32_t k, int32_t* indices,
                  int64_t max_row_len, void* workspace, size_t workspace_bytes,
                  hipStream_t stream);
+
+/* Decode form that allocates nothing, for callers that cannot call hipMalloc
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same selection as topk_decode with a NULL workspace, but
+ * the multi-workgroup tier keeps its state in a fixed per-GPU scratch array
+ * of the library (24 MiB, held from library load until process exit) instead
+ * of a caller workspace or the library's slab.  Plans whose workspace would
+ * exceed it give TOPK_EWORKSPACE (no decode plan on a 256-compute-unit GPU
+ * does).  The first call on a GPU clears the array with a kernel on
+ * `stream`; every call returns it to zero.  Every call on one GPU shares that
+ * GPU's array: calls that overlap on one GPU (different streams, without
+ * ordering between them) race and their results are undefined.  A row
+ * barrier that gives up is counted by topk_status, whose reset also re-zeroes
+ * the array. */
+int topk_decode_noalloc(const float* logits, int64_t row_stride, const int32_t* n_valid,
+                        int32_t num_rows, int32_t k, int32_t* indices, hipStream_t stream);
 
 /* ---- Output options -------------------------------------------------------
  * Same selection as topk_decode / topk_prefill, with:
