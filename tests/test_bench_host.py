@@ -46,3 +46,27 @@ def test_traffic_is_reported_only_for_the_sources_it_was_taken_on():
         else:
             assert got is None
     assert b.traffic_for("no_such_workload") is None
+
+
+def test_headline_is_the_prefill_tile_and_every_workload_is_in_the_line():
+    b = _bench()
+    assert b.HEADLINE == 3
+    import workloads
+    assert workloads.config(b.HEADLINE).name == "prefill_causal_4096x16640_k1024"
+    cfgs = sorted({c for c, _ in b.EXTRA} | {b.HEADLINE})
+    assert cfgs == [1, 2, 3, 4, 5]
+    assert {kw.get("bs") for c, kw in b.EXTRA if c == 4} == {1, 8}
+
+
+def test_latency_samples_do_not_depend_on_steps():
+    b = _bench()
+    for steps in (1, 5, 20, 50, 199):
+        assert b.latency_samples(steps) >= 200
+    assert b.latency_samples(1000) == 1000
+
+
+def test_rotation_reads_a_gib_between_reuses():
+    b = _bench()
+    for read in (65536, 459852, 15339924 - 4 * 2048 * 64 - 256, 133700640, 8388608):
+        n = b.rotation(read)
+        assert (n - 1) * read >= b.ROTATE_BYTES
