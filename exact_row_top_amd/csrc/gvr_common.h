@@ -17,6 +17,12 @@ constexpr int kBins = 2048;
 // final refine).
 constexpr int kSingleCap = 2048;
 
+// One-workgroup tier: the row's K output indices are staged in LDS and
+// written with coalesced stores; the crossing bin's members (key, index)
+// share that 16 KiB area, so their cap is (16 KiB - 4 K) / 8 members (1792,
+// 1536, 1024 for K = 512, 1024, 2048).
+constexpr int one_wg_cap(int k) { return (2 * kSingleCap * 4 - 4 * k) / 8; }
+
 // The pages' rescue trigger is a crossing bin of more than
 // min(CS x 4096, 32 x K, 16384) members with CS workgroups per row
 // (PR 20998 "What changes").  Here the crossing-bin members of a row go

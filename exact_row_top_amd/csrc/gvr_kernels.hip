@@ -57,14 +57,19 @@ namespace ert {
 // The kernel
 // ---------------------------------------------------------------------------
 
-template <int BLOCK>
+template <int K, int BLOCK>
 struct alignas(16) Smem {
   union {
     uint32_t hist[kBins + 64];  // + one trash word per lane for NaN markers
-    struct {
+    struct {                    // split tier: the row's member list (last workgroup)
       uint32_t key[kSingleCap];
       int32_t idx[kSingleCap];
     } c;
+    struct {                    // one-workgroup tier: the staged output row and the
+      int32_t ob[K];            // crossing bin's members
+      uint32_t key[one_wg_cap(K)];
+      int32_t idx[one_wg_cap(K)];
+    } o;
   } u;
   uint32_t dh[256];
   uint32_t mm[2 * (BLOCK / 64)];  // per-wave class extremes of a radix level
@@ -103,7 +108,7 @@ __global__ void __launch_bounds__(BLOCK)
   constexpr int NSB = K / 64;             // sample blocks
   constexpr int SPW = (NSB + W - 1) / W;  // sample blocks per wave
   constexpr int NW = (QPT * 4 + 31) / 32;
-  __shared__ Smem<BLOCK> sm;
+  __shared__ Smem<K, BLOCK> sm;
 
   const int t = threadIdx.x;
   const int G = SPLIT ? p.wgs_per_row : 1;
@@ -454,7 +459,7 @@ __global__ void __launch_bounds__(BLOCK)
         }
         __syncthreads();
         cr = crossing_1sync<BLOCK>(sm.u.hist, (uint32_t)K, sm.scan);
-        path = (cr.b >= 0 && cr.m <= (uint32_t)kSingleCap) ? 1 : 3;
+        path = (cr.b >= 0 && cr.m <= (uint32_t)one_wg_cap(K)) ? 1 : 3;
       };
       verify(false);
       if (path == 3 && cr.b == kBins - 1) {
@@ -549,7 +554,11 @@ __global__ void __launch_bounds__(BLOCK)
             bits &= bits - 1u;
             // (the slot is clamped, not tested: the winners number exactly
             // cr.above <= K)
-            out[min(wpos, (uint32_t)K - 1u)] = base + (i & ~3) * BLOCK + (i & 3);
+            // (staged in LDS: stored straight from the walk, each winner was
+            // its own scattered 4-byte write, and on the prefill tile those
+            // writes kept the compute units' address units busy while the
+            // rows' loads queued behind them)
+            sm.u.o.ob[min(wpos, (uint32_t)K - 1u)] = base + (i & ~3) * BLOCK + (i & 3);
             ++wpos;
           }
         }
@@ -565,9 +574,9 @@ __global__ void __launch_bounds__(BLOCK)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const bool c = (cq >> (3 - e)) & 1u;
-              if (c && cpos < (uint32_t)kSingleCap) {
-                sm.u.c.key[cpos] = fkey(v[j][e]);
-                sm.u.c.idx[cpos] = (q << 2) + e - lead;
+              if (c && cpos < (uint32_t)one_wg_cap(K)) {
+                sm.u.o.key[cpos] = fkey(v[j][e]);
+                sm.u.o.idx[cpos] = (q << 2) + e - lead;
               }
               cpos += c ? 1u : 0u;
             }
@@ -577,13 +586,22 @@ __global__ void __launch_bounds__(BLOCK)
       __syncthreads();
       // ---- refine (a7) ----------------------------------------------------
       const uint32_t m = cr.m;
+      int32_t* const ob = sm.u.o.ob;
       if (need == m) {
-        for (uint32_t i = t; i < m; i += BLOCK) out[cr.above + i] = sm.u.c.idx[i];
+        for (uint32_t i = t; i < m; i += BLOCK) ob[cr.above + i] = sm.u.o.idx[i];
       } else if (m <= (uint32_t)kRankMax) {
-        rank_select<BLOCK>(sm.u.c.key, sm.u.c.idx, m, need, out, cr.above);
+        rank_select<BLOCK>(sm.u.o.key, sm.u.o.idx, m, need, ob, cr.above);
       } else {
-        list_select<BLOCK>(sm.u.c.key, sm.u.c.idx, m, need, p.deterministic != 0, out, cr.above,
+        list_select<BLOCK>(sm.u.o.key, sm.u.o.idx, m, need, p.deterministic != 0, ob, cr.above,
                            (uint32_t)K, sm.dh, &sm.cross, sm.scan, sm.mm, sm.ctr, nbar);
+      }
+      __syncthreads();
+      // ---- output (a9): the staged row, coalesced -------------------------
+      if ((reinterpret_cast<uintptr_t>(out) & 15u) == 0u) {
+        for (int i = 4 * t; i < K; i += 4 * BLOCK)
+          *reinterpret_cast<int4*>(out + i) = *reinterpret_cast<const int4*>(ob + i);
+      } else {
+        for (int i = t; i < K; i += BLOCK) out[i] = ob[i];
       }
       put_stats(path, (int)cr.m, (int)cr.above, cr.b);
       return;

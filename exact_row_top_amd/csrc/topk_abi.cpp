@@ -100,7 +100,7 @@ int make_plan(int32_t num_rows, int64_t env_len, int32_t k, int32_t force_g, int
     p.rows_per_launch = num_rows;
     p.launches = num_rows > 0 ? 1 : 0;
     p.ws_bytes = 0;
-    p.cap = kSingleCap;
+    p.cap = one_wg_cap(k);
   } else {
     const int64_t per_part = (Qmax + G - 1) / G;
     int qpt = 0, block = 0;
