@@ -186,11 +186,18 @@ class Runner:
         else:
             self.bmax = None
         self.out = torch.empty((w.num_rows, w.k), dtype=torch.int32, device="cuda")
+        self.read_floor = False
+        self.sink = torch.zeros(1, dtype=torch.int32, device="cuda")
         self.ws = ert.new_workspace(w.num_rows, w.row_stride, w.k)
         torch.cuda.synchronize()
 
     def step(self, i, copy=None):
         c = (i % self.ncopies) if copy is None else copy
+        if self.read_floor:
+            self.ert.read_floor(self.copies[c], self.ext[0], self.w.k,
+                                extents2=self.ext[1] if len(self.ext) > 1 else None,
+                                sink=self.sink)
+            return
         kw = dict(self.kw)
         if self.bmax is not None:
             kw["bmax"] = self.bmax[c]
@@ -353,6 +360,10 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="only the chosen workload (no other workloads, no tail protocol)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline leg")
+    ap.add_argument("--read-floor", action="store_true",
+                    help="time the read floor instead of the selection: a launch that reads "
+                         "exactly the scores the selection reads, in its launch shape, and "
+                         "nothing else (a measurement aid)")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches instead of a graph replay (for counter runs)")
     ap.add_argument("--copy-calib", action="store_true",
@@ -416,6 +427,9 @@ def main():
                         "row_bytes_per_launch": w.algorithmic_bytes()}
         else:
             bsk_info = {"path": "ordinary"}
+    run.read_floor = args.read_floor
+    if args.read_floor:
+        w.name += "_read_floor"
     log(f"[bench] {run.ncopies} rotating copies ({run.bytes_resident() / 2**20:.0f} MiB, "
         f"{run.ncopies * read_bytes_of(w) / 2**20:.0f} MiB of scores read per rotation)")
     t0 = time.perf_counter()
@@ -472,12 +486,13 @@ def main():
             "unit": "GB/s",
             "frac": head["frac"],
             "traffic": traffic_for(w.name),
-            "kernel": ("topk_blockskip_kernel" if bsk_info and "blocks_visited" in bsk_info
+            "kernel": ("read_floor_kernel" if args.read_floor else
+                       "topk_blockskip_kernel" if bsk_info and "blocks_visited" in bsk_info
                        else "gvr_topk_kernel"),
             "kernel_source_hash": kernel_hash(),
         },
     }
-    if not args.no_extra and args.workload == HEADLINE:
+    if not args.no_extra and args.workload == HEADLINE and not args.read_floor:
         extra = {}
         for cfg, kw in EXTRA:
             we = workloads.config(cfg, **kw)

@@ -94,6 +94,8 @@ def load_library():
     lib.topk_workspace_init.restype = ctypes.c_int
     lib.topk_decode_noalloc.argtypes = [P, I64, P, I32, I32, P, P]
     lib.topk_decode_noalloc.restype = ctypes.c_int
+    lib.topk_read_floor.argtypes = [I32, P, I64, P, P, I32, I32, P, P]
+    lib.topk_read_floor.restype = ctypes.c_int
     lib.topk_status.argtypes = [P, P]
     lib.topk_status.restype = ctypes.c_int
     lib.topk_strerror.argtypes = [ctypes.c_int]
@@ -449,6 +451,22 @@ def status(device="cuda", stream=None):
     out = torch.zeros(1, dtype=torch.int32, device=device)
     _check(load_library().topk_status(out.data_ptr(), _stream_ptr(stream, out.device)))
     return out
+
+
+def read_floor(logits, extents, k: int, extents2=None, *, sink=None, stream=None):
+    """Measurement aid: read exactly the scores a selection of these rows would
+    read, in its launch shape, and nothing else (decode: extents = n_valid;
+    prefill: extents, extents2 = row_starts, row_ends)."""
+    import torch
+    rows, row_stride = _logits_layout(logits)
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=logits.device)
+    mode = 0 if extents2 is None else 1
+    _check(load_library().topk_read_floor(
+        mode, logits.data_ptr(), row_stride, extents.data_ptr(),
+        extents2.data_ptr() if extents2 is not None else None, rows, int(k), sink.data_ptr(),
+        _stream_ptr(stream, logits.device)))
+    return sink
 
 
 def new_workspace(num_rows: int, row_stride: int, k: int, device="cuda", stream=None):

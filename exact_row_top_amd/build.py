@@ -17,7 +17,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libexact_row_top.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["gvr_kernels.hip", "blockskip.hip", "epilogue.hip", "state.hip", "topk_abi.cpp"]
+SOURCES = ["gvr_kernels.hip", "blockskip.hip", "epilogue.hip", "state.hip", "calib.hip",
+           "topk_abi.cpp"]
 
 # -ffp-contract=off: the histogram bin is one definition evaluated in several
 #   passes; no pass may fuse it differently.

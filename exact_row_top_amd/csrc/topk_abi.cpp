@@ -19,6 +19,7 @@ const void* block_max_kernel_ptr();
 hipError_t state_timeout_address(uint32_t** out);
 hipError_t state_scratch_address(void** out);
 const void* fill_zero_kernel_ptr();
+const void* read_floor_kernel_ptr(int block, int qpt);
 const void* status_read_kernel_ptr();
 const void* status_reset_kernel_ptr();
 }
@@ -643,6 +644,56 @@ const char* topk_strerror(int status) {
     case TOPK_ELAUNCH: return "HIP launch or allocation failed";
     default: return "unknown status";
   }
+}
+
+int topk_read_floor(int32_t mode, const float* logits, int64_t row_stride, const int32_t* extents,
+                    const int32_t* extents2, int32_t num_rows, int32_t k, uint32_t* sink,
+                    hipStream_t stream) {
+  if (mode != 0 && mode != 1) return TOPK_EINVAL;
+  int rc = validate(mode, logits, row_stride, extents, extents2, num_rows, k, sink, 0);
+  if (rc != TOPK_OK || num_rows == 0) return rc;
+  std::lock_guard<std::mutex> lock(g_mu);
+  DevInfo* d = nullptr;
+  int dev = 0;
+  rc = device_info(&d, &dev);
+  if (rc != TOPK_OK) return rc;
+  // the plan the selection would take (block-skip and streaming forms aside)
+  Plan pl;
+  rc = make_plan(num_rows, row_stride, k, 0, (int64_t)1 << 40, &pl);
+  if (rc != TOPK_OK) return rc;
+  if (pl.G > 1) {
+    const int64_t cap = (int64_t)d->cus * d->occ[kidx(k)][qidx(pl.qpt)];
+    rc = make_plan(num_rows, row_stride, k, 0, cap, &pl);
+    if (rc != TOPK_OK) return rc;
+  }
+  const void* kern = read_floor_kernel_ptr(pl.block, pl.qpt);
+  if (!kern) return TOPK_EINVAL;
+  GvrParams prm;
+  memset(&prm, 0, sizeof(prm));
+  prm.logits = logits;
+  prm.row_stride = row_stride;
+  prm.n_valid = mode == 0 ? extents : nullptr;
+  prm.row_starts = mode == 1 ? extents : nullptr;
+  prm.row_ends = mode == 1 ? extents2 : nullptr;
+  prm.wgs_per_row = pl.G;
+  int32_t kk = k;
+  for (int64_t r0 = 0; r0 < num_rows; r0 += pl.rows_per_launch) {
+    const int64_t nr = (num_rows - r0) < pl.rows_per_launch ? (num_rows - r0) : pl.rows_per_launch;
+    prm.row_begin = (int32_t)r0;
+    prm.rows = (int32_t)nr;
+    int64_t grid;
+    if (pl.G == 1) {
+      prm.xcd_group = 0;
+      grid = nr;
+    } else {
+      prm.xcd_group = (pl.xcd_group && nr >= 8) ? 1 : 0;
+      grid = prm.xcd_group ? ((nr + 7) / 8) * 8 * pl.G : nr * pl.G;
+    }
+    void* args[] = {&prm, &kk, &sink};
+    if (hipLaunchKernel(kern, dim3((unsigned)grid), dim3(pl.block), args, 0, stream) != hipSuccess)
+      return TOPK_ELAUNCH;
+  }
+  return hipGetLastError() == hipSuccess ? TOPK_OK : TOPK_ELAUNCH;
 }
 
 int topk_plan_query(int32_t num_rows, int64_t row_stride, int64_t max_row_len, int32_t k,

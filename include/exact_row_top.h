@@ -361,6 +361,20 @@ int topk_device_query(int64_t* out);
  * suffix counts, out[5] = the crossing-bin member list).  Returns a status. */
 int topk_workspace_layout(int64_t* out);
 
+/* Measurement aid (not a selection): reads exactly the scores the selection
+ * of the same call would read -- the windows of rows longer than k, as
+ * aligned float4 groups -- in the launch shape the selection's plan uses
+ * (one workgroup per row, or G per row with the same part split), and does
+ * nothing else with them.  Its time is the floor the row reads alone set
+ * under the selection's time.  mode 0: decode (extents = n_valid); mode 1:
+ * prefill (extents = row_starts, extents2 = row_ends).  sink: device
+ * uint32[1], written only on a data-dependent condition that keeps the loads.
+ * Block-skip and streaming forms are not modelled.  Status as for
+ * topk_decode. */
+int topk_read_floor(int32_t mode, const float* logits, int64_t row_stride, const int32_t* extents,
+                    const int32_t* extents2, int32_t num_rows, int32_t k, uint32_t* sink,
+                    hipStream_t stream);
+
 /* Host-side argument validation exactly as the entry points run it (no device
  * access).  mode: 0 decode (extents = n_valid, extents2 unused), 1 prefill. */
 int topk_validate(int32_t mode, const void* logits, int64_t row_stride, const void* extents,

@@ -222,3 +222,11 @@ def test_options_reject_negative_barrier_spins():
     lib = ert.load_library()
     rc = lib.topk_decode_ex(P16, 4096, P16, 4, 512, P16, None, 0, None, ctypes.pointer(o))
     assert rc == ert.TOPK_EINVAL
+
+
+def test_read_floor_validates_on_the_host():
+    lib = ert.load_library()
+    assert lib.topk_read_floor(2, P16, 4096, P16, P16, 4, 512, P16, None) == ert.TOPK_EINVAL
+    assert lib.topk_read_floor(0, P16, 4096, P16, None, 4, 100, P16, None) == ert.TOPK_EINVAL
+    assert lib.topk_read_floor(0, P16 + 4, 4096, P16, None, 4, 512, P16, None) == ert.TOPK_ELAYOUT
+    assert lib.topk_read_floor(1, P16, 4096, P16, P16, 0, 512, None, None) == 0  # empty
