@@ -461,6 +461,34 @@ const void* blockskip_kernel(int k, bool self) {
   }
 }
 
-const void* block_max_kernel_ptr() { return reinterpret_cast<const void*>(&block_max_kernel); }
+// The same maxima with coalesced loads (16-byte aligned rows of a multiple of
+// 4 floats): eight lanes per block of 32, one 16-byte load each, so a wave
+// reads 1 KiB of consecutive scores per load; a 3-step exchange finds each
+// block's maximum.
+__global__ void __launch_bounds__(256) block_max_vec_kernel(const float* logits, int64_t row_stride,
+                                                            int32_t num_rows, float* bmax,
+                                                            int64_t bmax_stride) {
+  const int64_t nb = (row_stride + 31) / 32;
+  const int64_t gb = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 3;  // this lane's block
+  const int sub = (int)(threadIdx.x & 7u);
+  const int64_t r = gb / nb, i = gb - r * nb;
+  float m = __builtin_nanf("");
+  if (r < num_rows) {
+    const int64_t col = i * 32 + sub * 4;
+    if (col < row_stride) {  // (row_stride % 4 == 0: the whole float4 lies in the row)
+      const f4 x = *reinterpret_cast<const f4*>(logits + r * row_stride + col);
+      m = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    }
+  }
+  m = fmaxf(m, __shfl_xor(m, 1, 64));
+  m = fmaxf(m, __shfl_xor(m, 2, 64));
+  m = fmaxf(m, __shfl_xor(m, 4, 64));
+  if (r < num_rows && sub == 0) bmax[r * bmax_stride + i] = m;
+}
+
+const void* block_max_kernel_ptr(bool vec) {
+  return vec ? reinterpret_cast<const void*>(&block_max_vec_kernel)
+             : reinterpret_cast<const void*>(&block_max_kernel);
+}
 
 }  // namespace ert

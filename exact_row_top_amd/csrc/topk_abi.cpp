@@ -15,7 +15,7 @@ namespace ert {
 const void* gvr_kernel(int k, int block, int qpt, bool split);
 const void* epilogue_kernel(int k);
 const void* blockskip_kernel(int k, bool self);
-const void* block_max_kernel_ptr();
+const void* block_max_kernel_ptr(bool vec);
 hipError_t state_timeout_address(uint32_t** out);
 hipError_t state_scratch_address(void** out);
 const void* fill_zero_kernel_ptr();
@@ -549,13 +549,16 @@ int topk_block_max(const float* logits, int64_t row_stride, int32_t num_rows, fl
   const int64_t nb = (row_stride + 31) / 32;
   if (bmax_stride < nb) return TOPK_EINVAL;
   if (!aligned(logits, 4) || !aligned(bmax, 4)) return TOPK_ELAYOUT;
+  // coalesced 16-byte loads (eight lanes per block) when the layout allows
+  const bool vec = aligned(logits, 16) && (row_stride % 4) == 0;
   const int64_t total = (int64_t)num_rows * nb;
-  const int64_t grid = (total + 255) / 256;
+  const int64_t per_wg = vec ? 32 : 256;  // blocks of 32 per workgroup of 256
+  const int64_t grid = (total + per_wg - 1) / per_wg;
   if (grid >= ((int64_t)1 << 31)) return TOPK_EINVAL;
   int32_t nr = num_rows;
   void* args[] = {const_cast<float**>(&logits), &row_stride, &nr, &bmax, &bmax_stride};
-  if (hipLaunchKernel(block_max_kernel_ptr(), dim3((unsigned)grid), dim3(256), args, 0, stream) !=
-      hipSuccess)
+  if (hipLaunchKernel(block_max_kernel_ptr(vec), dim3((unsigned)grid), dim3(256), args, 0,
+                      stream) != hipSuccess)
     return TOPK_ELAUNCH;
   if (hipGetLastError() != hipSuccess) return TOPK_ELAUNCH;
   return TOPK_OK;

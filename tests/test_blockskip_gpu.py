@@ -45,9 +45,12 @@ def _run(ert, w, dev, bm, **kw):
     return got.cpu().numpy(), st.cpu().numpy()
 
 
-def test_block_max_producer(ert):
+@pytest.mark.parametrize("stride", [1000, 1001, 4096])
+def test_block_max_producer(ert, stride):
+    # stride % 4 == 0 takes the coalesced producer, 1001 the per-block one;
+    # 1000 and 1001 end on a partial block
     import torch
-    w = workloads.random_decode(5, 1000, [1000, 999, 37, 0, 640], 512, seed=3)
+    w = workloads.random_decode(5, stride, [stride, 999, 37, 0, 640], 512, seed=3)
     w.logits[1, 64:96] = np.nan  # a whole NaN block
     w.logits[2, 100] = np.inf
     x = torch.from_numpy(w.logits).cuda()
