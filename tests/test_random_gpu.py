@@ -12,7 +12,7 @@ from gpu_helpers import log, run_gpu
 pytestmark = pytest.mark.gpu
 
 DISTS = ("normal", "uniform", "levels4", "two_valued", "signed_zero", "hidden_peak", "ramp_up",
-         "ramp_down", "neg_inf", "all_equal", "huge", "tiny")
+         "ramp_down", "neg_inf", "pos_inf", "all_equal", "huge", "tiny")
 
 
 @pytest.fixture(scope="module")
