@@ -49,6 +49,9 @@ PEAK_HBM_GBS = 8000.0  # MI355X published HBM3E bandwidth
 ROTATE_BYTES = 1 << 30  # scores read between two reads of one copy
 FLUSH_BYTES = 1 << 30   # fill before each cold sample and before the timed region
 MIN_LATENCY_SAMPLES = 200
+# GPU sleep queued ahead of a timed region's start event (about 1 ms): long
+# enough for the host to submit the region's launches behind it
+SUBMIT_SLEEP_CYCLES = int(3e6)
 HEADLINE = 3
 EXTRA = ((1, {}), (2, {}), (4, {"bs": 1}), (4, {"bs": 8}), (5, {}))
 TAIL_RATIO_LIMIT = 4.0  # tie-heavy kinds alone: p50 at most this times the 64-level row's
@@ -223,6 +226,10 @@ def measure(torch, run: Runner, steps: int, warmup: int, flush_buf, eager: bool 
     def region(launch_all):
         flush(torch, flush_buf)
         torch.cuda.synchronize()
+        # a GPU sleep ahead of the start event: the launches are queued
+        # before the GPU reaches the event, so the region holds their
+        # execution only, not the host's submission of the first ones
+        torch.cuda._sleep(SUBMIT_SLEEP_CYCLES)
         t_start.record()
         launch_all()
         t_end.record()
@@ -242,9 +249,8 @@ def measure(torch, run: Runner, steps: int, warmup: int, flush_buf, eager: bool 
         return g
 
     if eager:
-        # K launches issued one by one behind a GPU sleep (counter runs)
+        # K launches issued one by one (counter runs)
         def eager_all():
-            torch.cuda._sleep(int(20e6))
             for i in range(steps):
                 run.step(warmup + i)
         region_us = region(eager_all)
@@ -276,6 +282,7 @@ def measure(torch, run: Runner, steps: int, warmup: int, flush_buf, eager: bool 
     if warm_graph:
         gw = graph_of(lambda: [run.step(0, copy=0) for _ in range(steps)])
         torch.cuda.synchronize()
+        torch.cuda._sleep(SUBMIT_SLEEP_CYCLES)
         t_start.record()
         gw.replay()
         t_end.record()
@@ -345,7 +352,7 @@ def tail_protocol(torch, ert, workloads, steps, flush_buf):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=HEADLINE,
                     help="1..5 (3, the prefill tile, is the headline); 6 = workload 2's shape "
