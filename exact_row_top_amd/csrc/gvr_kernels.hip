@@ -263,15 +263,19 @@ __global__ void __launch_bounds__(BLOCK)
   // the wave holding the part's last group) read zeros without a memory
   // access and become markers below.  The whole offset sits in the per-lane
   // offset, which the range check covers.
+  // Every one of the QPT loads is issued, also past the part's end (those
+  // read zeros without a memory access and no pass looks at them): with a
+  // fixed count of loads behind the sample's, the waits for the sample (and
+  // for a group) are exact counts, so the bracket and, in the split tier,
+  // the sample's floor run while the part is still in flight.
   f4 v[QPT];
   {
     const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(base, q1 * 16);
     const int vo = (qw0 + l) * 16;
 #pragma unroll
     for (int j = 0; j < QPT; ++j)
-      if (j < nj)
-        v[j] = __builtin_bit_cast(
-            f4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, vo + j * BLOCK * 16, 0, kCachePolicyNT));
+      v[j] = __builtin_bit_cast(
+          f4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, vo + j * BLOCK * 16, 0, kCachePolicyNT));
   }
   // Visit this thread's groups; `full` (uniform per wave) says all 64 lanes
   // hold four in-window scores, so only boundary waves pay for NaN checks.
@@ -372,9 +376,10 @@ __global__ void __launch_bounds__(BLOCK)
                           __builtin_isfinite(range) && __builtin_isfinite(bm.sc4) &&
                           __builtin_isfinite(bm.c04) && (bm.sc > 0.0f) && !p.force_rescue;
 
-  // The lead / tail lanes become NaN markers only now, after the bracket,
-  // so the sample reduction does not wait for the whole part to arrive.
-  {
+  // The lead / tail lanes become NaN markers only after the bracket (and in
+  // the split tier after the sample's floor), so that work does not wait
+  // for the whole part to arrive.
+  auto mark_ends = [&]() {
     // first group of the window (lead lanes): q == 0 is thread 0's j == 0
     if (q0 == 0 && t == 0 && lead > 0) {
 #pragma unroll
@@ -403,7 +408,7 @@ __global__ void __launch_bounds__(BLOCK)
           }
       }
     }
-  }
+  };
 
   int floor_bin = -1;  // split tier: the floor bin its histogram counts from
   auto put_stats = [&](int path, int m, int above, int b) {
@@ -425,6 +430,7 @@ __global__ void __launch_bounds__(BLOCK)
   Cross cr{-1, 0u, 0u, 0u};
 
   float xf = -__builtin_inff();  // one-workgroup retry: the counted scores' floor
+  if (!SPLIT) mark_ends();
   if (!SPLIT) {
     // ==== one workgroup per row ============================================
     if (bracket_ok) {
@@ -677,6 +683,7 @@ __global__ void __launch_bounds__(BLOCK)
       __syncthreads();
       path = sm.ctr[3] ? 3 : 1;
     }
+    mark_ends();
     // One verify round: the part's scores >= edge(bl) counted per bin in
     // LDS, merged into gh (zero on entry) through the workspace behind a row
     // barrier, the crossing bin -> cr.  Returns the path: 1 fast, 3 crowded
