@@ -96,6 +96,11 @@ __global__ void __launch_bounds__(kBskBlock) topk_blockskip_kernel(const GvrPara
   const float qnan = __builtin_nanf("");
 
   const f4* win4 = reinterpret_cast<const f4*>(win);
+  // Raw buffer over the window's float4 groups: a group past the window reads
+  // zeros without a memory access, so every load below is issued
+  // unconditionally and the waits for them are exact counts (loads under a
+  // lane condition would be waited for one by one).
+  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(win4, ((nv + 3) & ~3) * 4);
   if (SELF) {
     // ---- first pass: every block once, its maximum kept in LDS -----------
     // (streaming rows of up to kBskCap blocks; U loads in flight per lane)
@@ -106,9 +111,9 @@ __global__ void __launch_bounds__(kBskBlock) topk_blockskip_kernel(const GvrPara
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int sb = s0 + u * W * 8 + (l >> 3);
-        const int q = sb * 32 + sub * 4;
-        x[u] = f4{-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
-        if (sb < nb && q < nv) x[u] = __builtin_nontemporal_load(win4 + (q >> 2));
+        const int q = sb * 32 + sub * 4;  // (q >= nv: out of the buffer's range)
+        x[u] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(wrs, q * 4, 0,
+                                                                             kCachePolicyNT));
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -271,11 +276,11 @@ __global__ void __launch_bounds__(kBskBlock) topk_blockskip_kernel(const GvrPara
         if (s < nwalk) {
           const int b = nlist < 0 ? s : (int)sm.list[s];
           const int q = b * 32 + sub * 4;
-          if (q < nv) {
-            p0[u] = q;
-            x[u] = win4[q >> 2];
-          }
+          if (q < nv) p0[u] = q;
         }
+        // (no block, or past the window: an offset out of the buffer's range)
+        const int off = p0[u] >= 0 ? p0[u] * 4 : ((nv + 3) & ~3) * 4;
+        x[u] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(wrs, off, 0, 0));
       }
 #pragma unroll
       for (int u = 0; u < U; ++u)
