@@ -49,6 +49,10 @@ int64_t quads_for(int64_t env_len) { return (env_len + 3 + 3) / 4; }
 // Work to fill the chip: about 512 wave quartets (256-thread groups) in
 // flight.
 constexpr int64_t kFillUnits = 512;
+// Split tier: the part size (float4 groups) the planner aims at.
+constexpr int64_t kSplitPart = 2048;
+// Compute units per XCD on MI355X (256 units in 8 XCDs).
+constexpr int64_t kCusPerXcd = 32;
 
 // Launch shape for (rows, envelope, k).  `capacity` = workgroups the device
 // keeps resident at once for the split kernel (only the split tier needs its
@@ -76,14 +80,26 @@ int make_plan(int32_t num_rows, int64_t env_len, int32_t k, int32_t force_g, int
     G = 1;  // rows short enough for the smallest workgroup: splitting costs more
             // in cross-workgroup latency than it gains in bandwidth
   } else {
+    // Parts of about kSplitPart float4 groups, as many as fill the chip
+    // (kFillUnits workgroups in all), never more than the largest part needs.
+    // Measured on MI355X (cold launches): 8 rows x 262144 at K = 2048 run
+    // 39.1 us with 32 parts of 2048 groups against 43.8 with 64 of 1024;
+    // 8 rows x 114963 at K = 512 17.8-18.3 us with 8-16 parts against 20.5
+    // with 33 small ones; 64 rows x 131072 keep 8 parts (more would need a
+    // second launch or add merge work: 23.1 us at 12 parts, 21.9 at 8).
     const int64_t part_max =
         (int64_t)kSplitVariants[kNumSplit - 1].block * kSplitVariants[kNumSplit - 1].qpt;
     const int64_t g_min = (Qmax + part_max - 1) / part_max;
     const int64_t g_fill = (kFillUnits + num_rows - 1) / (num_rows > 0 ? num_rows : 1);
-    // never parts below 4 groups per thread
-    const int64_t part_min = (int64_t)kSplitVariants[0].block * kSplitVariants[0].qpt;
-    const int64_t g_useful = (Qmax + part_min - 1) / part_min;
+    const int64_t g_useful = (Qmax + kSplitPart - 1) / kSplitPart;
     int64_t gg = g_fill < g_useful ? g_fill : g_useful;
+    // A launch of eight or more rows maps each row's workgroups onto one XCD
+    // (kCusPerXcd compute units): while the rows there leave every unit at
+    // most one workgroup, a part never shares a unit, and the row does not
+    // wait for a part that did (8 rows x 262144, K = 2048: 36.5 us with 32
+    // parts, 40.1 with 33).
+    const int64_t g_xcd = kCusPerXcd / ((num_rows + 7) / 8);
+    if (g_xcd >= g_min && gg > g_xcd) gg = g_xcd;
     if (gg > kMaxWgsPerRow) gg = kMaxWgsPerRow;  // larger parts then
     if (gg < g_min) gg = g_min;
     if (gg < 1) gg = 1;
@@ -106,7 +122,10 @@ int make_plan(int32_t num_rows, int64_t env_len, int32_t k, int32_t force_g, int
     const int64_t per_part = (Qmax + G - 1) / G;
     int qpt = 0, block = 0;
     for (const Variant& sv : kSplitVariants)
-      if ((int64_t)sv.block * sv.qpt >= per_part) {
+      // parts over 1024 groups take the 512-thread shape (eight waves to
+      // hide a part's latency, as measured above) rather than 256 x 8
+      if ((int64_t)sv.block * sv.qpt >= per_part &&
+          !(sv.block == 256 && sv.qpt == 8 && per_part > 1024)) {
         qpt = sv.qpt;
         block = sv.block;
         break;

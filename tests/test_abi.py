@@ -125,12 +125,17 @@ def test_plans_for_the_workloads():
         assert p["wgs_per_row"] > 1 and p["block"] in (256, 512)
         assert p["wgs_per_row"] * p["quads_per_thread"] * p["block"] >= (stride + 6) // 4
         assert p["cap"] == 2048
-    # few rows of 262144: more parts than the split tier allows would be
-    # useful, so the plan takes the most it allows with larger parts
+    # few rows of 262144: parts of about 2048 float4 groups in the 512-thread
+    # shape, no more than the compute units of the row's XCD (32)
     for rows, k in ((1, 2048), (7, 512), (2, 1024)):
         p = ert.plan_query(rows, 262144, k)
-        assert p["wgs_per_row"] == 64
-        assert 64 * p["quads_per_thread"] * p["block"] >= (262144 + 6) // 4
+        assert p["wgs_per_row"] == 32 and p["block"] == 512
+        assert 32 * p["quads_per_thread"] * p["block"] >= (262144 + 6) // 4
+    # the longest row a plan holds needs all 64 parts of the largest shape
+    p = ert.plan_query(1, 64 * 9 * 512 * 4 - 16, 512)
+    assert p["wgs_per_row"] == 64 and p["block"] == 512 and p["quads_per_thread"] == 9
+    # rows that already fill the chip keep the fewest parts the shape allows
+    assert ert.plan_query(64, 131072, 2048)["wgs_per_row"] == 8
     # capacity bounds rows per launch (co-resident split workgroups)
     p = ert.plan_query(64, 131072, 2048, cu_count=16, wgs_per_cu=2)
     assert p["rows_per_launch"] * p["wgs_per_row"] <= 32 and p["launches"] > 1

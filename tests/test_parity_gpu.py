@@ -175,20 +175,20 @@ def test_tiers_and_rescue_agree(ert, k, dist):
         assert_parity(w, got, want)
 
 
-# ---- few very long rows: the plan's most parts, each larger ---------------------------
+# ---- few very long rows: many parts per row --------------------------------------
 
 @pytest.mark.parametrize("k,rows,stride,dist", [
     (2048, 1, 262144, "normal"), (512, 3, 262144, "hidden_peak"), (1024, 2, 262144, "ramp_down"),
     (512, 1, 64 * 9 * 512 * 4 - 16, "normal")])
 def test_few_very_long_rows(ert, k, rows, stride, dist):
-    # (fewer rows than fill the chip at one part per 1024 groups: the plan
-    # takes 64 parts of the larger shapes; the last case is near the longest
-    # row any plan holds)
+    # (fewer rows than fill the chip: 32 parts of about 2048 groups per row of
+    # 262144, one per compute unit of an XCD; the last case is near the
+    # longest row any plan holds, which takes all 64 parts)
     nv = [stride - 3 * r for r in range(rows)]
     w = workloads.random_decode(rows, stride, nv, k, seed=rows + k, dist=dist)
     p = ert.plan_query(rows, stride, k)
     log(f"[very long] k={k} rows={rows} stride={stride} {dist} G={p['wgs_per_row']}")
-    assert p["wgs_per_row"] == 64
+    assert p["wgs_per_row"] == (32 if stride == 262144 else 64)
     got = run_gpu(w)
     assert_parity(w, got)
 
