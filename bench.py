@@ -55,9 +55,11 @@ SUBMIT_SLEEP_CYCLES = int(3e6)
 HEADLINE = 3
 EXTRA = ((1, {}), (2, {}), (4, {"bs": 1}), (4, {"bs": 8}), (5, {}))
 TAIL_RATIO_LIMIT = 4.0  # tie-heavy kinds alone: p50 at most this times the 64-level row's
+# the kernels and the planner that shapes their launches (the counters depend
+# on both)
 KERNEL_SOURCES = ("exact_row_top_amd/csrc/gvr_kernels.hip", "exact_row_top_amd/csrc/gvr_common.h",
                   "exact_row_top_amd/csrc/gvr_device.h", "exact_row_top_amd/csrc/row_window.h",
-                  "exact_row_top_amd/csrc/blockskip.hip")
+                  "exact_row_top_amd/csrc/blockskip.hip", "exact_row_top_amd/csrc/topk_abi.cpp")
 
 
 def log(*a):
