@@ -80,8 +80,9 @@ int make_plan(int32_t num_rows, int64_t env_len, int32_t k, int32_t force_g, int
     G = 1;  // rows short enough for the smallest workgroup: splitting costs more
             // in cross-workgroup latency than it gains in bandwidth
   } else {
-    // Parts of about kSplitPart float4 groups, as many as fill the chip
-    // (kFillUnits workgroups in all), never more than the largest part needs.
+    // Parts of about kSplitPart float4 groups, but no more parts than fill
+    // the chip (kFillUnits workgroups in all), and at least as many as the
+    // largest part shape needs.
     // Measured on MI355X (cold launches): 8 rows x 262144 at K = 2048 run
     // 39.1 us with 32 parts of 2048 groups against 43.8 with 64 of 1024;
     // 8 rows x 114963 at K = 512 17.8-18.3 us with 8-16 parts against 20.5
@@ -93,11 +94,13 @@ int make_plan(int32_t num_rows, int64_t env_len, int32_t k, int32_t force_g, int
     const int64_t g_fill = (kFillUnits + num_rows - 1) / (num_rows > 0 ? num_rows : 1);
     const int64_t g_useful = (Qmax + kSplitPart - 1) / kSplitPart;
     int64_t gg = g_fill < g_useful ? g_fill : g_useful;
-    // A launch of eight or more rows maps each row's workgroups onto one XCD
-    // (kCusPerXcd compute units): while the rows there leave every unit at
-    // most one workgroup, a part never shares a unit, and the row does not
-    // wait for a part that did (8 rows x 262144, K = 2048: 36.5 us with 32
-    // parts, 40.1 with 33).
+    // At most one part per compute unit of an XCD (kCusPerXcd units) for the
+    // rows an XCD holds: a launch of eight or more rows maps each row's
+    // workgroups onto one XCD, so a part then never shares a unit and the
+    // row does not wait for a part that did (8 rows x 262144, K = 2048:
+    // 36.5 us with 32 parts, 40.1 with 33); fewer rows spread their parts
+    // over the XCDs, where the cap costs nothing (2 rows x 262144: 19.4 us
+    // at 32 parts against 22.7 at 64).
     const int64_t g_xcd = kCusPerXcd / ((num_rows + 7) / 8);
     if (g_xcd >= g_min && gg > g_xcd) gg = g_xcd;
     if (gg > kMaxWgsPerRow) gg = kMaxWgsPerRow;  // larger parts then
