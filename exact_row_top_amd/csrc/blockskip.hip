@@ -168,16 +168,7 @@ __global__ void __launch_bounds__(kBskBlock) topk_blockskip_kernel(const GvrPara
   }
   bmin = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(bmin)));
   btop = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(btop)));
-  auto make_map = [](float a, float b, BinMap& m) {
-    const float range = b - a;
-    m.gmin = a;
-    m.sc = (float)kBins / range;
-    m.c0 = -a * m.sc;
-    m.sc4 = 4.0f * m.sc;
-    m.c04 = 4.0f * m.c0;
-    return __builtin_isfinite(a) && __builtin_isfinite(b) && (b > a) && __builtin_isfinite(range) &&
-           __builtin_isfinite(m.sc4) && __builtin_isfinite(m.c04) && (m.sc > 0.0f);
-  };
+  auto make_map = [](float a, float b, BinMap& m) { return m.set(a, b); };
   float xf = -__builtin_inff();
   bool crowd = false;
   {

@@ -74,27 +74,42 @@ __device__ __forceinline__ float sgpr_f32(float x) {
   return x;
 }
 
-// The bracket's bin map: bin(x) = trunc(clamp(fma(x, sc, c0), 0, kBins - 1))
-// with sc = kBins / (gmax - gmin) and c0 = -gmin * sc, each rounded once per
-// row.  A fused multiply-add is monotone non-decreasing in x, so equal values
-// share a bin and bins ascend with the value; this is the single definition
-// every step uses.  The same map scaled by 4 (exact: a power-of-two scale)
-// gives a bin's LDS byte offset directly.  The final masks only matter for
-// NaN (outside the contract): they keep the LDS index in range.
+// The bracket's bin map over [lo, hi]: with sc4 = 4 kBins / (hi - lo) and
+// cm = 2^23 - lo * sc4 (each rounded once per row), t = fma(x, sc4, cm)
+// clamped to [2^23, 2^23 + 4 (kBins - 1)] is a float whose unit in the last
+// place is 1, so t is a whole number and its low 23 bits are t - 2^23: bin(x)
+// is that number divided by 4 and rounded down, and the bin's LDS byte offset
+// is the same bits with the low two cleared -- one mask, no float-to-integer
+// conversion.  The fused multiply-add, the clamp and the mask are each
+// monotone non-decreasing in x, so equal values share a bin and bins ascend
+// with the value; this is the single definition every step uses.  Folding
+// 2^23 into the addend shifts the partition by at most half a unit of cm: a
+// fraction of a bin unless the bracket is narrower than about 1e-6 of its
+// magnitude, where bins merge (the selection stays exact; a crowded bin takes
+// the rescue).  The mask also keeps a NaN's index in range (NaN scores are
+// outside the contract).
 struct BinMap {
-  float gmin, sc, c0, sc4, c04;
-  float top4 = sgpr_f32(4.0f * (kBins - 1));  // vbin_off's clamp bound
+  float gmin, sc, sc4, cm;
+  float lo23 = sgpr_f32(8388608.0f);                        // 2^23
+  float hi23 = sgpr_f32(8388608.0f + 4.0f * (kBins - 1));  // 2^23 + the top bin's offset
+  // the map of [lo, hi]; false when the bracket cannot carry one
+  __device__ __forceinline__ bool set(float lo, float hi) {
+    const float range = hi - lo;
+    gmin = lo;
+    sc = (float)kBins / range;
+    sc4 = 4.0f * sc;
+    cm = __builtin_fmaf(-lo, sc4, 8388608.0f);
+    return __builtin_isfinite(lo) && __builtin_isfinite(hi) && (hi > lo) &&
+           __builtin_isfinite(range) && __builtin_isfinite(sc4) && __builtin_isfinite(cm) &&
+           (sc > 0.0f);
+  }
 };
-__device__ __forceinline__ int vbin(float x, const BinMap& bm) {
-  float t = __builtin_fmaf(x, bm.sc, bm.c0);
-  t = __builtin_amdgcn_fmed3f(t, 0.0f, (float)(kBins - 1));
-  return ((int)t) & (kBins - 1);
-}
 __device__ __forceinline__ uint32_t vbin_off(float x, const BinMap& bm) {
-  float t = __builtin_fmaf(x, bm.sc4, bm.c04);
-  t = __builtin_amdgcn_fmed3f(t, 0.0f, bm.top4);
-  return ((uint32_t)(int)t) & (uint32_t)(4 * kBins - 4);
+  float t = __builtin_fmaf(x, bm.sc4, bm.cm);
+  t = __builtin_amdgcn_fmed3f(t, bm.lo23, bm.hi23);
+  return __float_as_uint(t) & (uint32_t)(4 * kBins - 4);
 }
+__device__ __forceinline__ int vbin(float x, const BinMap& bm) { return (int)(vbin_off(x, bm) >> 2); }
 // One lane's float4 group against the crossing bin's edges [xlo, xhi) (both
 // uniform): its four winner bits (x >= xhi) are shifted into wacc and its
 // four member bits (xlo <= x < xhi) into cacc, each by add-with-carry
@@ -487,7 +502,11 @@ __device__ __forceinline__ float bin_edge(int b, const BinMap& bm) {
   uint32_t hi = 0xFF800000u;  // key(+inf): vbin = kBins - 1 >= b
   const uint32_t l = (uint32_t)lane_id();
   {
-    const float est = bm.gmin + (float)b / bm.sc;
+    // bin b starts where fma(x, sc4, cm) rounds to 2^23 + 4 b or more, at
+    // x = (2^23 - cm + 4 b - 1/2) / sc4 (2^23 - cm is exact while the
+    // bracket's lower end lies within 512 widths of zero; elsewhere the
+    // search below finds the edge all the same)
+    const float est = ((8388608.0f - bm.cm) + (4.0f * (float)b - 0.5f)) / bm.sc4;
     const uint32_t c = fkey(est);
     const int64_t pk = (int64_t)c - 31 + (int64_t)l;
     const uint32_t probe =

@@ -365,16 +365,8 @@ __global__ void __launch_bounds__(BLOCK)
       gmax = fmaxf(gmax, hh);
     }
   }
-  const float range = gmax - gmin;
   BinMap bm;
-  bm.gmin = gmin;
-  bm.sc = (float)kBins / range;
-  bm.c0 = -gmin * bm.sc;
-  bm.sc4 = 4.0f * bm.sc;
-  bm.c04 = 4.0f * bm.c0;
-  const bool bracket_ok = __builtin_isfinite(gmin) && __builtin_isfinite(gmax) && (gmax > gmin) &&
-                          __builtin_isfinite(range) && __builtin_isfinite(bm.sc4) &&
-                          __builtin_isfinite(bm.c04) && (bm.sc > 0.0f) && !p.force_rescue;
+  const bool bracket_ok = bm.set(gmin, gmax) && !p.force_rescue;
 
   // The lead / tail lanes become NaN markers only after the bracket (and in
   // the split tier after the sample's floor), so that work does not wait
@@ -492,18 +484,11 @@ __global__ void __launch_bounds__(BLOCK)
         for (int i = 1; i < W; ++i) top = fmaxf(top, sm.hmax[i]);
         top = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(top)));
         const float lo = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sm.thr[0])));
-        const float sc = (float)kBins / (top - lo);
-        const float c0 = -lo * sc;
-        if (__builtin_isfinite(lo) && __builtin_isfinite(top) && top > lo &&
-            __builtin_isfinite(top - lo) && __builtin_isfinite(4.0f * sc) &&
-            __builtin_isfinite(4.0f * c0) && sc > 0.0f) {
+        BinMap rm;
+        if (rm.set(lo, top)) {
           gmin = lo;
           gmax = top;
-          bm.gmin = lo;
-          bm.sc = sc;
-          bm.c0 = c0;
-          bm.sc4 = 4.0f * sc;
-          bm.c04 = 4.0f * c0;
+          bm = rm;
           xf = lo;
           for (int i = t; i < kBins + 64; i += BLOCK) sm.u.hist[i] = 0u;
           __syncthreads();
@@ -549,23 +534,37 @@ __global__ void __launch_bounds__(BLOCK)
       // thread's score i = 32 d + nd - 1 - p (group i / 4, lane i % 4)
       auto nbits = [&](int d) { return 4 * min(max(ngrp - 8 * d, 0), 8); };
       {
-        uint32_t wpos = ex & 0xFFFFu;
+        // (staged in LDS: stored straight from the walk, each winner was its
+        // own scattered 4-byte write, and on the prefill tile those writes
+        // kept the compute units' address units busy while the rows' loads
+        // queued behind them)
+        // The slots need no bound: every winner lies in a bin above the
+        // crossing one (the edge is exact), so the winners number at most
+        // cr.above <= K.
+        constexpr uint32_t kLogBlock = BLOCK == 256 ? 8u : BLOCK == 512 ? 9u : 10u;
+        static_assert(BLOCK == 256 || BLOCK == 512 || BLOCK == 1024, "power-of-two workgroups");
+        uint32_t wo = (ex & 0xFFFFu) * 4u;  // byte offset of the next slot
         const int base = ((q0 + t) << 2) - lead;
 #pragma unroll
         for (int d = 0; d < NW; ++d) {
-          const int top = 32 * d + nbits(d) - 1;
-          uint32_t bits = wb[d];
+          const int nb = nbits(d);  // uniform
+          if (nb == 0) break;
+          // left-aligned, the word's leading-zero count c is the score's
+          // place in it: group 8 d + c / 4, lane c % 4
+          uint32_t bits = wb[d] << (32 - nb);
+          const int bd = base + 32 * d * BLOCK;
           while (bits) {
-            const int i = top - __builtin_ctz(bits);
-            bits &= bits - 1u;
-            // (the slot is clamped, not tested: the winners number exactly
-            // cr.above <= K)
-            // (staged in LDS: stored straight from the walk, each winner was
-            // its own scattered 4-byte write, and on the prefill tile those
-            // writes kept the compute units' address units busy while the
-            // rows' loads queued behind them)
-            sm.u.o.ob[min(wpos, (uint32_t)K - 1u)] = base + (i & ~3) * BLOCK + (i & 3);
-            ++wpos;
+            const uint32_t c = (uint32_t)__builtin_clz(bits);
+            bits ^= 0x80000000u >> c;
+            // (the loop tests the cleared word itself, not a copy of the old
+            // one against the bit)
+            asm volatile("" : "+v"(bits));
+            // lane c % 4 and group c / 4, whose stride 4 BLOCK is c's bits
+            // 2..4 shifted up by log2(BLOCK): both fields from one shift-or
+            *reinterpret_cast<int32_t*>(reinterpret_cast<char*>(sm.u.o.ob) + wo) =
+                bd + (int)(((c << kLogBlock) | c) & ((0x1Cu << kLogBlock) | 3u));
+            wo += 4u;
+            asm volatile("" : "+v"(wo));
           }
         }
       }
@@ -812,18 +811,11 @@ __global__ void __launch_bounds__(BLOCK)
         row_barrier(hdr, G, nbar, p.sync);
         const uint32_t tk = __builtin_amdgcn_readfirstlane(load_agent(&hdr->cand_cur));
         const float top = tk ? from_key(tk) : -__builtin_inff();
-        const float sc = (float)kBins / (top - lo);
-        const float c0 = -lo * sc;
-        if (__builtin_isfinite(lo) && __builtin_isfinite(top) && top > lo &&
-            __builtin_isfinite(top - lo) && __builtin_isfinite(4.0f * sc) &&
-            __builtin_isfinite(4.0f * c0) && sc > 0.0f) {
+        BinMap rm;
+        if (rm.set(lo, top)) {
           gmin = lo;
           gmax = top;
-          bm.gmin = lo;
-          bm.sc = sc;
-          bm.c0 = c0;
-          bm.sc4 = 4.0f * sc;
-          bm.c04 = 4.0f * c0;
+          bm = rm;
           xfloor = lo;
           retry = true;
         }
