@@ -86,7 +86,7 @@ __global__ void __launch_bounds__(kBskBlock) topk_blockskip_kernel(const GvrPara
 
   // ---- short row: identity then -1 ----------------------------------------
   if (nv <= K) {
-    for (int i = t; i < K; i += BLOCK) out[i] = (i < nv) ? i : -1;
+    for (int i = t; i < K; i += BLOCK) store_nt(out + i, (i < nv) ? i : -1);
     if (stats && t < kStatsWords) stats[t] = (t == 0) ? 0 : (t == 6 ? 1 : (t == 7 ? kBskMembers : -1));
     return;
   }
@@ -335,7 +335,7 @@ __global__ void __launch_bounds__(kBskBlock) topk_blockskip_kernel(const GvrPara
       const bool win_ = x >= xhi;
       const bool mem = !win_ && x >= xlo;
       const uint32_t wp = wave_append(win_, &sm.ctr[0]);
-      if (win_ && wp < (uint32_t)K) out[wp] = pos;
+      if (win_ && wp < (uint32_t)K) store_nt(out + wp, pos);
       const uint32_t mp = wave_append(mem, &sm.ctr[1]);
       if (mem && mp < (uint32_t)kBskMembers) {
         sm.key[mp] = fkey(x);
@@ -347,7 +347,7 @@ __global__ void __launch_bounds__(kBskBlock) topk_blockskip_kernel(const GvrPara
     __syncthreads();
     const uint32_t m = cr.m, need = (uint32_t)K - cr.above;
     if (need == m) {
-      for (uint32_t i = t; i < m; i += BLOCK) out[cr.above + i] = sm.idx[i];
+      for (uint32_t i = t; i < m; i += BLOCK) store_nt(out + cr.above + i, sm.idx[i]);
     } else if (m <= (uint32_t)kRankMax) {
       rank_select<BLOCK>(sm.key, sm.idx, m, need, out, cr.above);
     } else {
@@ -408,9 +408,9 @@ __global__ void __launch_bounds__(kBskBlock) topk_blockskip_kernel(const GvrPara
         eq = d == s.thr && (!pick || ((~(uint32_t)pos) >> s2.shift) >= s2.thr);
       }
       const uint32_t gp = wave_append(gt, &sm.ctr[0]);
-      if (gt && gp < eqbase) out[gp] = pos;
+      if (gt && gp < eqbase) store_nt(out + gp, pos);
       const uint32_t tk = wave_append(eq, &sm.ctr[1]);
-      if (eq && tk < s.rem) out[eqbase + tk] = pos;
+      if (eq && tk < s.rem) store_nt(out + eqbase + tk, pos);
     });
   }
   if (stats && t == 0) {

@@ -146,7 +146,7 @@ __global__ void __launch_bounds__(BLOCK)
 
   // ---- short row (a1): identity then -1 ----------------------------------
   if (nv <= K) {
-    for (int i = g * BLOCK + t; i < K; i += G * BLOCK) out[i] = (i < nv) ? i : -1;
+    for (int i = g * BLOCK + t; i < K; i += G * BLOCK) store_nt(out + i, (i < nv) ? i : -1);
     if (stats && g == 0 && t < kStatsWords)
       stats[t] = (t == 0) ? 0 : (t == 6 ? G : (t == 7 ? p.cap : -1));
     return;
@@ -541,28 +541,18 @@ __global__ void __launch_bounds__(BLOCK)
         // The slots need no bound: every winner lies in a bin above the
         // crossing one (the edge is exact), so the winners number at most
         // cr.above <= K.
-        constexpr uint32_t kLogBlock = BLOCK == 256 ? 8u : BLOCK == 512 ? 9u : 10u;
-        static_assert(BLOCK == 256 || BLOCK == 512 || BLOCK == 1024, "power-of-two workgroups");
         uint32_t wo = (ex & 0xFFFFu) * 4u;  // byte offset of the next slot
         const int base = ((q0 + t) << 2) - lead;
 #pragma unroll
         for (int d = 0; d < NW; ++d) {
           const int nb = nbits(d);  // uniform
           if (nb == 0) break;
-          // left-aligned, the word's leading-zero count c is the score's
-          // place in it: group 8 d + c / 4, lane c % 4
           uint32_t bits = wb[d] << (32 - nb);
           const int bd = base + 32 * d * BLOCK;
           while (bits) {
-            const uint32_t c = (uint32_t)__builtin_clz(bits);
-            bits ^= 0x80000000u >> c;
-            // (the loop tests the cleared word itself, not a copy of the old
-            // one against the bit)
-            asm volatile("" : "+v"(bits));
-            // lane c % 4 and group c / 4, whose stride 4 BLOCK is c's bits
-            // 2..4 shifted up by log2(BLOCK): both fields from one shift-or
+            const uint32_t c = walk_pop(bits);
             *reinterpret_cast<int32_t*>(reinterpret_cast<char*>(sm.u.o.ob) + wo) =
-                bd + (int)(((c << kLogBlock) | c) & ((0x1Cu << kLogBlock) | 3u));
+                bd + walk_offset<BLOCK>(c);
             wo += 4u;
             asm volatile("" : "+v"(wo));
           }
@@ -604,9 +594,9 @@ __global__ void __launch_bounds__(BLOCK)
       // ---- output (a9): the staged row, coalesced -------------------------
       if ((reinterpret_cast<uintptr_t>(out) & 15u) == 0u) {
         for (int i = 4 * t; i < K; i += 4 * BLOCK)
-          *reinterpret_cast<int4*>(out + i) = *reinterpret_cast<const int4*>(ob + i);
+          store_nt4(out + i, ob + i);
       } else {
-        for (int i = t; i < K; i += BLOCK) out[i] = ob[i];
+        for (int i = t; i < K; i += BLOCK) store_nt(out + i, ob[i]);
       }
       put_stats(path, (int)cr.m, (int)cr.above, cr.b);
       return;
@@ -905,7 +895,7 @@ __global__ void __launch_bounds__(BLOCK)
               if (c && cpos < m) {
                 const int32_t idx = (q << 2) + e - lead;
                 if (direct) {
-                  out[above + cpos] = idx;
+                  store_nt(out + above + cpos, idx);
                 } else {
                   float x = v[j][e];
                   asm volatile("" : "+v"(x));
@@ -928,14 +918,15 @@ __global__ void __launch_bounds__(BLOCK)
         const int base = ((q0 + t) << 2) - lead;
 #pragma unroll
         for (int d = 0; d < NW; ++d) {
-          const int top = 32 * d + nbits(d) - 1;
-          uint32_t bits = wb[d];
+          const int nb = nbits(d);  // uniform
+          if (nb == 0) break;
+          uint32_t bits = wb[d] << (32 - nb);
+          const int bd = base + 32 * d * BLOCK;
           while (bits) {
-            const int i = top - __builtin_ctz(bits);
-            bits &= bits - 1u;
+            const uint32_t c = walk_pop(bits);
             // (the slot is clamped, not tested: the row's winners number
             // exactly `above` <= K)
-            out[min(wpos, (uint32_t)K - 1u)] = base + (i & ~3) * BLOCK + (i & 3);
+            store_nt(out + min(wpos, (uint32_t)K - 1u), bd + walk_offset<BLOCK>(c));
             ++wpos;
           }
         }
@@ -1045,8 +1036,8 @@ __global__ void __launch_bounds__(BLOCK)
         const int32_t idx = (q << 2) + e - lead;
         const bool gt = d > thr2;
         const bool eq = d == thr2 && kept(idx);
-        if (gt && gpos < (uint32_t)K) out[gpos] = idx;
-        if (eq && tk < s.rem) out[eqbase + tk] = idx;
+        if (gt && gpos < (uint32_t)K) store_nt(out + gpos, idx);
+        if (eq && tk < s.rem) store_nt(out + eqbase + tk, idx);
         gpos += gt ? 1u : 0u;
         tk += eq ? 1u : 0u;
       }
