@@ -183,6 +183,36 @@ __device__ __forceinline__ void group_bits(const f4& x, float xlo, float xhi, ui
       : "scc");
 }
 
+// The winner bits of group_bits alone, and the member lane masks g[e]
+// (xlo <= x[e] < xhi) handed back in scalar registers instead of being
+// shifted into a second word: members are rare, so a group with none costs
+// three scalar ors and a branch (append_members below takes the others).
+__device__ __forceinline__ void group_wins(const f4& x, float xlo, float xhi, uint32_t& wacc,
+                                           uint64_t (&g)[4]) {
+  uint64_t h0, h1, h2, h3, cy;
+  asm("v_cmp_ge_f32_e64 %[h0], %[x0], %[hi]\n\t"
+      "v_cmp_ge_f32_e64 %[h1], %[x1], %[hi]\n\t"
+      "v_cmp_ge_f32_e64 %[h2], %[x2], %[hi]\n\t"
+      "v_cmp_ge_f32_e64 %[h3], %[x3], %[hi]\n\t"
+      "v_cmp_ge_f32_e64 %[g0], %[x0], %[lo]\n\t"
+      "v_cmp_ge_f32_e64 %[g1], %[x1], %[lo]\n\t"
+      "v_cmp_ge_f32_e64 %[g2], %[x2], %[lo]\n\t"
+      "v_cmp_ge_f32_e64 %[g3], %[x3], %[lo]\n\t"
+      "s_andn2_b64 %[g0], %[g0], %[h0]\n\t"
+      "s_andn2_b64 %[g1], %[g1], %[h1]\n\t"
+      "s_andn2_b64 %[g2], %[g2], %[h2]\n\t"
+      "s_andn2_b64 %[g3], %[g3], %[h3]\n\t"
+      "v_addc_co_u32_e64 %[w], %[cy], %[w], %[w], %[h0]\n\t"
+      "v_addc_co_u32_e64 %[w], %[cy], %[w], %[w], %[h1]\n\t"
+      "v_addc_co_u32_e64 %[w], %[cy], %[w], %[w], %[h2]\n\t"
+      "v_addc_co_u32_e64 %[w], %[cy], %[w], %[w], %[h3]"
+      : [w] "+v"(wacc), [h0] "=&s"(h0), [h1] "=&s"(h1), [h2] "=&s"(h2), [h3] "=&s"(h3),
+        [g0] "=&s"(g[0]), [g1] "=&s"(g[1]), [g2] "=&s"(g[2]), [g3] "=&s"(g[3]), [cy] "=&s"(cy)
+      : [x0] "v"(x[0]), [x1] "v"(x[1]), [x2] "v"(x[2]), [x3] "v"(x[3]), [hi] "s"(xhi),
+        [lo] "s"(xlo)
+      : "scc");
+}
+
 // LDS histogram word at a byte offset from vbin_off.
 __device__ __forceinline__ uint32_t* hword(uint32_t* h, uint32_t off) {
   return reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(h) + off);
@@ -373,6 +403,41 @@ __device__ __forceinline__ uint32_t wave_offsets(uint32_t v, uint32_t* ctr) {
     base = __hip_atomic_fetch_add(ctr, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   base = (uint32_t)__builtin_amdgcn_readlane((int)base, 63);
   return base + inc - v;
+}
+
+// One group's members (the lane masks g[e] of group_wins, not all zero; a
+// uniform branch) appended to the LDS member list: one workgroup-scope add
+// per wave reserves their slots in the high half of *ctr (whose low half
+// wave_offsets uses for the winners), then each member lane writes its key
+// and position, pos0 + e.  Slots at or past cap are dropped (the row then
+// holds more members than the list, which the caller has ruled out).
+__device__ __forceinline__ void append_members(const f4& x, int pos0, const uint64_t (&g)[4],
+                                               uint32_t* ctr, uint32_t* key, int32_t* idx,
+                                               uint32_t cap) {
+  uint32_t n[4], tot = 0u;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    n[e] = (uint32_t)__popcll(g[e]);
+    tot += n[e];
+  }
+  const int f = __ffsll((unsigned long long)__ballot(1)) - 1;
+  uint32_t b = 0u;
+  if (lane_id() == f)
+    b = __hip_atomic_fetch_add(ctr, tot << 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  b = (uint32_t)__builtin_amdgcn_readlane((int)b, f) >> 16;
+  const uint32_t l = (uint32_t)lane_id();
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if ((g[e] >> l) & 1ull) {
+      const uint32_t s = b + __builtin_amdgcn_mbcnt_hi((uint32_t)(g[e] >> 32),
+                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)g[e], 0u));
+      if (s < cap) {
+        key[s] = fkey(x[e]);
+        idx[s] = pos0 + e;
+      }
+    }
+    b += n[e];
+  }
 }
 
 template <int BLOCK>

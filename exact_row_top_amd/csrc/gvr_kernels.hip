@@ -509,27 +509,28 @@ __global__ void __launch_bounds__(BLOCK)
       }
       __syncthreads();
       const uint32_t need = (uint32_t)K - cr.above;
-      uint32_t wb[NW], cb[NW];
+      uint32_t wb[NW];
 #pragma unroll
-      for (int i = 0; i < NW; ++i) wb[i] = cb[i] = 0u;
-      // this thread's winner (x >= x_hi) and member (x_lo <= x < x_hi) bits,
-      // shifted in group by group
+      for (int i = 0; i < NW; ++i) wb[i] = 0u;
+      // this thread's winner bits (x >= x_hi), shifted in group by group;
+      // members (x_lo <= x < x_hi) go to the LDS list as they are met
       int ngrp = 0;  // groups this wave visited (uniform)
       {
         const float xlo = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sm.thr[0])));
         const float xhi = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sm.thr[1])));
         each([&](int j, int q, bool) {
-          group_bits(v[j], xlo, xhi, wb[j >> 3], cb[j >> 3]);
+          uint64_t gm[4];
+          group_wins(v[j], xlo, xhi, wb[j >> 3], gm);
+          if ((gm[0] | gm[1] | gm[2] | gm[3]) != 0ull)
+            append_members(v[j], (q << 2) - lead, gm, &sm.bc[0], sm.u.o.key, sm.u.o.idx,
+                           (uint32_t)one_wg_cap(K));
           ngrp = j + 1;
         });
       }
-      uint32_t nwin = 0, ncand = 0;
+      uint32_t nwin = 0;
 #pragma unroll
-      for (int i = 0; i < NW; ++i) {
-        nwin += __popc(wb[i]);
-        ncand += __popc(cb[i]);
-      }
-      const uint32_t ex = wave_offsets((ncand << 16) | nwin, &sm.bc[0]);
+      for (int i = 0; i < NW; ++i) nwin += __popc(wb[i]);
+      const uint32_t ex = wave_offsets(nwin, &sm.bc[0]);
       // word d holds groups 8d .. 8d + 7, nd bits shifted in: bit p is this
       // thread's score i = 32 d + nd - 1 - p (group i / 4, lane i % 4)
       auto nbits = [&](int d) { return 4 * min(max(ngrp - 8 * d, 0), 8); };
@@ -557,26 +558,6 @@ __global__ void __launch_bounds__(BLOCK)
             asm volatile("" : "+v"(wo));
           }
         }
-      }
-      // (a wave without members skips the pass)
-      if (__any(ncand != 0u)) {
-        uint32_t cpos = ex >> 16;
-        each([&](int j, int q, bool) {
-          const int d = j >> 3;
-          const int sh = nbits(d) - 4 - 4 * (j - 8 * d);  // the group's lowest bit (score 3)
-          const uint32_t cq = (cb[d] >> sh) & 0xFu;
-          if (__any(cq != 0u)) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const bool c = (cq >> (3 - e)) & 1u;
-              if (c && cpos < (uint32_t)one_wg_cap(K)) {
-                sm.u.o.key[cpos] = fkey(v[j][e]);
-                sm.u.o.idx[cpos] = (q << 2) + e - lead;
-              }
-              cpos += c ? 1u : 0u;
-            }
-          }
-        });
       }
       __syncthreads();
       // ---- refine (a7) ----------------------------------------------------
