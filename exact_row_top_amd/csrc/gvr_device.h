@@ -92,13 +92,17 @@ struct BinMap {
   float gmin, sc, sc4, cm;
   float lo23 = sgpr_f32(8388608.0f);                        // 2^23
   float hi23 = sgpr_f32(8388608.0f + 4.0f * (kBins - 1));  // 2^23 + the top bin's offset
-  // the map of [lo, hi]; false when the bracket cannot carry one
+  // the map of [lo, hi] (both uniform); false when the bracket cannot carry one
   __device__ __forceinline__ bool set(float lo, float hi) {
     const float range = hi - lo;
     gmin = lo;
     sc = (float)kBins / range;
-    sc4 = 4.0f * sc;
-    cm = __builtin_fmaf(-lo, sc4, 8388608.0f);
+    // (uniform: scalar registers, which the histogram passes copy into a
+    // vector register where an instruction needs one, rather than holding a
+    // vector register for them across the row)
+    sc4 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(4.0f * sc)));
+    cm = __int_as_float(
+        __builtin_amdgcn_readfirstlane(__float_as_int(__builtin_fmaf(-lo, sc4, 8388608.0f))));
     return __builtin_isfinite(lo) && __builtin_isfinite(hi) && (hi > lo) &&
            __builtin_isfinite(range) && __builtin_isfinite(sc4) && __builtin_isfinite(cm) &&
            (sc > 0.0f);
@@ -314,79 +318,58 @@ __device__ __forceinline__ void rank_select(uint32_t* key, int32_t* idx, uint32_
 // Wave and block primitives
 // ---------------------------------------------------------------------------
 
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
-}
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
-}
+// Wave-wide scans and reductions as in-place DPP-fused instructions: each
+// step combines a lane with the lane that its row shift (within rows of 16)
+// or row broadcast (lane 15 / 31 into the following rows, row_mask) names.
+// Without bound_ctrl a lane whose source lies outside its row is not
+// written, which is what a scan (adding nothing) and an idempotent min / max
+// want: no lane test and no select per step, one instruction per value.  A
+// DPP read of a register that a vector instruction wrote needs two wait
+// states on gfx9: the s_nop 1 ahead of every step.  The inputs' own writers
+// are covered by the first step's s_nop as well.
+#define ERT_DPP_STEP1(OP, R, CTL, RMASK) \
+  "s_nop 1\n\t" OP " " R ", " R ", " R " " CTL " row_mask:" RMASK " bank_mask:0xf\n\t"
+#define ERT_DPP_STEP2(OPA, OPB, RA, RB, CTL, RMASK)                                  \
+  "s_nop 1\n\t" OPA " " RA ", " RA ", " RA " " CTL " row_mask:" RMASK " bank_mask:0xf\n\t" \
+  OPB " " RB ", " RB ", " RB " " CTL " row_mask:" RMASK " bank_mask:0xf\n\t"
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts
 // (within rows of 16) and the gfx9 row broadcasts (across rows).
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  const int l = lane_id();
-  const int rl = l & 15;
-  uint32_t s;
-  s = dpp_u32<0x111>(v);
-  v += (rl >= 1) ? s : 0u;
-  s = dpp_u32<0x112>(v);
-  v += (rl >= 2) ? s : 0u;
-  s = dpp_u32<0x114>(v);
-  v += (rl >= 4) ? s : 0u;
-  s = dpp_u32<0x118>(v);
-  v += (rl >= 8) ? s : 0u;
-  s = dpp_u32<0x142>(v);
-  v += ((l & 31) >= 16) ? s : 0u;
-  s = dpp_u32<0x143>(v);
-  v += (l >= 32) ? s : 0u;
+  asm(ERT_DPP_STEP1("v_add_u32_dpp", "%0", "row_shr:1", "0xf")
+      ERT_DPP_STEP1("v_add_u32_dpp", "%0", "row_shr:2", "0xf")
+      ERT_DPP_STEP1("v_add_u32_dpp", "%0", "row_shr:4", "0xf")
+      ERT_DPP_STEP1("v_add_u32_dpp", "%0", "row_shr:8", "0xf")
+      ERT_DPP_STEP1("v_add_u32_dpp", "%0", "row_bcast:15", "0xa")
+      ERT_DPP_STEP1("v_add_u32_dpp", "%0", "row_bcast:31", "0xc")
+      : "+v"(v));
   return v;
 }
 
-// Min and max over a wave (result in every lane, read from lane 63).  NaN
-// inputs are ignored by fminf / fmaxf.
+// Min and max over a wave (read from lane 63 into every lane).  A quiet NaN
+// (the kernels' markers) is ignored: in IEEE mode v_min / v_max return the
+// other operand.
 __device__ __forceinline__ void wave_minmax(float& mn, float& mx) {
-  const int l = lane_id();
-  const int rl = l & 15;
-  float a, b;
-#define ERT_STEP(CTRL, COND) \
-  a = dpp_f32<CTRL>(mn);     \
-  b = dpp_f32<CTRL>(mx);     \
-  if (COND) {                \
-    mn = fminf(mn, a);       \
-    mx = fmaxf(mx, b);       \
-  }
-  ERT_STEP(0x111, rl >= 1)
-  ERT_STEP(0x112, rl >= 2)
-  ERT_STEP(0x114, rl >= 4)
-  ERT_STEP(0x118, rl >= 8)
-  ERT_STEP(0x142, (l & 31) >= 16)
-  ERT_STEP(0x143, l >= 32)
-#undef ERT_STEP
+  asm(ERT_DPP_STEP2("v_min_f32_dpp", "v_max_f32_dpp", "%0", "%1", "row_shr:1", "0xf")
+      ERT_DPP_STEP2("v_min_f32_dpp", "v_max_f32_dpp", "%0", "%1", "row_shr:2", "0xf")
+      ERT_DPP_STEP2("v_min_f32_dpp", "v_max_f32_dpp", "%0", "%1", "row_shr:4", "0xf")
+      ERT_DPP_STEP2("v_min_f32_dpp", "v_max_f32_dpp", "%0", "%1", "row_shr:8", "0xf")
+      ERT_DPP_STEP2("v_min_f32_dpp", "v_max_f32_dpp", "%0", "%1", "row_bcast:15", "0xa")
+      ERT_DPP_STEP2("v_min_f32_dpp", "v_max_f32_dpp", "%0", "%1", "row_bcast:31", "0xc")
+      : "+v"(mn), "+v"(mx));
   mn = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mn), 63));
   mx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mx), 63));
 }
 
 // Largest of a and of b over a wave (result in every lane, from lane 63).
 __device__ __forceinline__ void wave_max2_u32(uint32_t& a, uint32_t& b) {
-  const int l = lane_id();
-  const int rl = l & 15;
-  uint32_t x, y;
-#define ERT_STEP(CTRL, COND) \
-  x = dpp_u32<CTRL>(a);      \
-  y = dpp_u32<CTRL>(b);      \
-  if (COND) {                \
-    a = max(a, x);           \
-    b = max(b, y);           \
-  }
-  ERT_STEP(0x111, rl >= 1)
-  ERT_STEP(0x112, rl >= 2)
-  ERT_STEP(0x114, rl >= 4)
-  ERT_STEP(0x118, rl >= 8)
-  ERT_STEP(0x142, (l & 31) >= 16)
-  ERT_STEP(0x143, l >= 32)
-#undef ERT_STEP
+  asm(ERT_DPP_STEP2("v_max_u32_dpp", "v_max_u32_dpp", "%0", "%1", "row_shr:1", "0xf")
+      ERT_DPP_STEP2("v_max_u32_dpp", "v_max_u32_dpp", "%0", "%1", "row_shr:2", "0xf")
+      ERT_DPP_STEP2("v_max_u32_dpp", "v_max_u32_dpp", "%0", "%1", "row_shr:4", "0xf")
+      ERT_DPP_STEP2("v_max_u32_dpp", "v_max_u32_dpp", "%0", "%1", "row_shr:8", "0xf")
+      ERT_DPP_STEP2("v_max_u32_dpp", "v_max_u32_dpp", "%0", "%1", "row_bcast:15", "0xa")
+      ERT_DPP_STEP2("v_max_u32_dpp", "v_max_u32_dpp", "%0", "%1", "row_bcast:31", "0xc")
+      : "+v"(a), "+v"(b));
   a = (uint32_t)__builtin_amdgcn_readlane((int)a, 63);
   b = (uint32_t)__builtin_amdgcn_readlane((int)b, 63);
 }
