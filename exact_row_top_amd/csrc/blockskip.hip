@@ -343,14 +343,14 @@ __global__ void __launch_bounds__(kBskBlock) topk_blockskip_kernel(const GvrPara
       }
     });
     __syncthreads();
-    if (t < 2) sm.ctr[t] = 0u;
-    __syncthreads();
     const uint32_t m = cr.m, need = (uint32_t)K - cr.above;
     if (need == m) {
       for (uint32_t i = t; i < m; i += BLOCK) store_nt(out + cr.above + i, sm.idx[i]);
     } else if (m <= (uint32_t)kRankMax) {
-      rank_select<BLOCK>(sm.key, sm.idx, m, need, out, cr.above);
+      rank_select_direct<BLOCK>(sm.key, sm.idx, m, need, out, cr.above);
     } else {
+      if (t < 2) sm.ctr[t] = 0u;
+      __syncthreads();
       list_select<BLOCK>(sm.key, sm.idx, m, need, p.deterministic != 0, out, cr.above, (uint32_t)K,
                          sm.dh, &sm.cross, sm.scan, sm.mm, sm.ctr, nbar);
     }

@@ -283,34 +283,31 @@ __device__ __forceinline__ uint32_t wave_append(bool pred, uint32_t* ctr) {
   return base + below;
 }
 
-// Rank-count selection of the `need` largest among m <= kRankMax candidates
-// held in LDS (key[], idx[]): a candidate's rank is the number with a larger
-// key, or an equal key and a smaller index; ranks below `need` go to
-// out[base + rank] (value descending, smallest index first inside a tie).
-// The arrays are padded to a multiple of 4 with keys that rank nothing.
+
+// The `need` largest of the m (key, index) pairs held in LDS (m small), by
+// rank counting: pair i's rank is the number of pairs with a larger key, or
+// an equal key and a smaller index, so ties go to the smallest indices.  No
+// barrier of its own (the list is complete and visible when it starts): the
+// tail of the last group of four is masked by position rather than padded,
+// and each pick goes straight to out[base + rank] (global memory), so no
+// wave waits for another once the list is built.
 template <int BLOCK>
-__device__ __forceinline__ void rank_select(uint32_t* key, int32_t* idx, uint32_t m, uint32_t need,
-                                            int32_t* out, uint32_t base) {
-  const int t = threadIdx.x;
-  const uint32_t m4 = (m + 3u) & ~3u;
-  if ((uint32_t)t >= m && (uint32_t)t < m4) {
-    key[t] = 0u;
-    idx[t] = 0x7FFFFFFF;
-  }
-  __syncthreads();
-  if ((uint32_t)t < m) {
-    const uint32_t kk = key[t];
-    const int32_t ii = idx[t];
+__device__ __forceinline__ void rank_select_direct(const uint32_t* key, const int32_t* idx,
+                                                   uint32_t m, uint32_t need, int32_t* out,
+                                                   uint32_t base) {
+  for (uint32_t i = threadIdx.x; i < m; i += BLOCK) {
+    const uint32_t kk = key[i];
+    const int32_t ii = idx[i];
     uint32_t rank = 0;
-    for (uint32_t j = 0; j < m4; j += 4) {
+    for (uint32_t j = 0; j < m; j += 4) {
       const uint4 kj = *reinterpret_cast<const uint4*>(key + j);
       const int4 ij = *reinterpret_cast<const int4*>(idx + j);
       rank += (kj.x > kk || (kj.x == kk && ij.x < ii)) ? 1u : 0u;
-      rank += (kj.y > kk || (kj.y == kk && ij.y < ii)) ? 1u : 0u;
-      rank += (kj.z > kk || (kj.z == kk && ij.z < ii)) ? 1u : 0u;
-      rank += (kj.w > kk || (kj.w == kk && ij.w < ii)) ? 1u : 0u;
+      rank += (j + 1 < m && (kj.y > kk || (kj.y == kk && ij.y < ii))) ? 1u : 0u;
+      rank += (j + 2 < m && (kj.z > kk || (kj.z == kk && ij.z < ii))) ? 1u : 0u;
+      rank += (j + 3 < m && (kj.w > kk || (kj.w == kk && ij.w < ii))) ? 1u : 0u;
     }
-    if (rank < need) out[base + rank] = ii;
+    if (rank < need) store_nt(out + base + rank, ii);
   }
 }
 
@@ -569,10 +566,10 @@ __device__ __forceinline__ Cross crossing_1sync(const uint32_t* h, uint32_t targ
 
 // Smallest score x (IEEE order over [-inf, +inf]) with vbin(x) >= b, so that
 // for every non-NaN x: vbin(x) >= b  <=>  x >= edge.  vbin is monotone in x,
-// so the set is an up-set.  The 64 lanes first probe the keys around the
-// arithmetic estimate gmin + b / sc (rounding puts the edge within a few
-// ulps of it); if the edge is not among them, a 64-way search over the keys
-// of -inf .. +inf (six rounds) finds it.  b <= 0 gives -inf; b >= kBins gives
+// so the set is an up-set.  The 64 lanes first probe the keys around an
+// arithmetic estimate of the edge (within an ulp of it for brackets near
+// zero); if the edge is not among them, a 64-way search over the keys of
+// -inf .. +inf (six rounds) finds it.  b <= 0 gives -inf; b >= kBins gives
 // NaN, which no score compares >= to.  Must be called by a whole wave.
 __device__ __forceinline__ float bin_edge(int b, const BinMap& bm) {
   if (b <= 0) return -__builtin_inff();

@@ -560,24 +560,34 @@ __global__ void __launch_bounds__(BLOCK)
         }
       }
       __syncthreads();
-      // ---- refine (a7) ----------------------------------------------------
+      // ---- output (a9) and refine (a7) ------------------------------------
+      // The winners staged by the walk go out with coalesced stores, and the
+      // refine writes its `need` picks straight to the output: no barrier
+      // follows, so no wave waits for these stores (a barrier waits for the
+      // wave's outstanding stores) or for another wave's refine.
       const uint32_t m = cr.m;
       int32_t* const ob = sm.u.o.ob;
-      if (need == m) {
-        for (uint32_t i = t; i < m; i += BLOCK) ob[cr.above + i] = sm.u.o.idx[i];
-      } else if (m <= (uint32_t)kRankMax) {
-        rank_select<BLOCK>(sm.u.o.key, sm.u.o.idx, m, need, ob, cr.above);
+      auto put_rows = [&](uint32_t b0, uint32_t b1) {  // ob[b0, b1) -> out, b0 % 4 == 0
+        if ((reinterpret_cast<uintptr_t>(out) & 15u) == 0u) {
+          const uint32_t e4 = b1 & ~3u;
+          for (uint32_t i = b0 + 4u * t; i < e4; i += 4u * BLOCK) store_nt4(out + i, ob + i);
+          if ((uint32_t)t < b1 - e4) store_nt(out + e4 + t, ob[e4 + t]);
+        } else {
+          for (uint32_t i = b0 + t; i < b1; i += BLOCK) store_nt(out + i, ob[i]);
+        }
+      };
+      if (need == m || m <= (uint32_t)kRankMax) {
+        put_rows(0u, cr.above);
+        if (need == m) {
+          for (uint32_t i = t; i < m; i += BLOCK) store_nt(out + cr.above + i, sm.u.o.idx[i]);
+        } else {
+          rank_select_direct<BLOCK>(sm.u.o.key, sm.u.o.idx, m, need, out, cr.above);
+        }
       } else {
         list_select<BLOCK>(sm.u.o.key, sm.u.o.idx, m, need, p.deterministic != 0, ob, cr.above,
                            (uint32_t)K, sm.dh, &sm.cross, sm.scan, sm.mm, sm.ctr, nbar);
-      }
-      __syncthreads();
-      // ---- output (a9): the staged row, coalesced -------------------------
-      if ((reinterpret_cast<uintptr_t>(out) & 15u) == 0u) {
-        for (int i = 4 * t; i < K; i += 4 * BLOCK)
-          store_nt4(out + i, ob + i);
-      } else {
-        for (int i = t; i < K; i += BLOCK) store_nt(out + i, ob[i]);
+        __syncthreads();
+        put_rows(0u, (uint32_t)K);
       }
       put_stats(path, (int)cr.m, (int)cr.above, cr.b);
       return;
@@ -933,7 +943,7 @@ __global__ void __launch_bounds__(BLOCK)
         }
         __syncthreads();
         if (m <= (uint32_t)kRankMax) {
-          rank_select<BLOCK>(sm.u.c.key, sm.u.c.idx, m, need, out, above);
+          rank_select_direct<BLOCK>(sm.u.c.key, sm.u.c.idx, m, need, out, above);
         } else {
           list_select<BLOCK>(sm.u.c.key, sm.u.c.idx, m, need, p.deterministic != 0, out, above,
                              (uint32_t)K, sm.dh, &sm.cross, sm.scan, sm.mm, sm.ctr, nbar);
