@@ -315,6 +315,16 @@ __device__ __forceinline__ void rank_select_direct(const uint32_t* key, const in
 // Wave and block primitives
 // ---------------------------------------------------------------------------
 
+// Workgroup barrier for LDS traffic only: the fences are scoped to LDS, so
+// the barrier waits for this wave's LDS operations (lgkmcnt) but not for its
+// global loads and stores, which may stay in flight across it (a kernel that
+// loads its next row during this one's selection relies on that).
+__device__ __forceinline__ void lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Wave-wide scans and reductions as in-place DPP-fused instructions: each
 // step combines a lane with the lane that its row shift (within rows of 16)
 // or row broadcast (lane 15 / 31 into the following rows, row_mask) names.
@@ -372,7 +382,7 @@ __device__ __forceinline__ void wave_max2_u32(uint32_t& a, uint32_t& b) {
 }
 
 // Exclusive prefix sum over the block in thread order; `total` gets the sum.
-// `sm` holds BLOCK/64 words.  Contains two __syncthreads.
+// `sm` holds BLOCK/64 words.  Contains two workgroup barriers.
 // Exclusive offsets of v over the whole workgroup in an arbitrary wave order:
 // a wave prefix sum and one LDS add per wave on *ctr (zero beforehand).  No
 // workgroup barrier.  Must be reached by the whole wave.
@@ -426,7 +436,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sm, ui
   const uint32_t inc = wave_incl_scan(v);
   const int w = threadIdx.x >> 6;
   if (lane_id() == 63) sm[w] = inc;
-  __syncthreads();
+  lds_sync();
   uint32_t off = 0, tot = 0;
 #pragma unroll
   for (int i = 0; i < W; ++i) {
@@ -434,7 +444,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sm, ui
     off += (i < w) ? s : 0u;
     tot += s;
   }
-  __syncthreads();
+  lds_sync();
   total = tot;
   return off + inc - v;
 }
@@ -499,7 +509,7 @@ __device__ __forceinline__ void find_crossing(Load&& load, uint32_t target, Cros
     out->m = 0;
     out->total = tot;
   }
-  __syncthreads();
+  lds_sync();
 }
 
 // The crossing over the kBins-word LDS histogram h with a single workgroup
@@ -528,7 +538,7 @@ __device__ __forceinline__ Cross crossing_1sync(const uint32_t* h, uint32_t targ
   const uint32_t s = owner_sum((int)threadIdx.x);
   const uint32_t inc = wave_incl_scan(s);
   if (l == 63) scan_sm[w] = inc;
-  __syncthreads();
+  lds_sync();
   uint32_t run = 0u, exw = 0u;
   int cw = -1;
 #pragma unroll
@@ -716,7 +726,7 @@ __device__ __forceinline__ RSel radix_select(Iter&& iter, uint32_t need, uint32_
   for (int L = 0; L < 4; ++L) {
     shift = 24 - 8 * L;
     for (int i = t; i < 256; i += BLOCK) dh[i] = 0u;
-    __syncthreads();
+    lds_sync();
     uint32_t kmax = 0u, knmin = 0u;  // the class's largest key, smallest complemented
     iter([&](uint32_t key) {
       const bool act = L == 0 || ((key ^ prefix) >> (shift + 8)) == 0u;
@@ -736,7 +746,7 @@ __device__ __forceinline__ RSel radix_select(Iter&& iter, uint32_t need, uint32_
         mm[W + w] = knmin;
       }
     }
-    __syncthreads();
+    lds_sync();
     if (EXT) {
 #pragma unroll
       for (int i = 0; i < W; ++i) {

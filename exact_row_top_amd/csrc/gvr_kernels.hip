@@ -100,41 +100,40 @@ struct WavesPerEu {
                                                               : 1;
 };
 
+// ---------------------------------------------------------------------------
+// One row in two halves: row_begin resolves the row and issues its loads
+// (the sample, then the part into v), row_finish selects.  The state the
+// loads leave for the selection travels in a RowCtx (uniform values).
+// ---------------------------------------------------------------------------
+
+template <int K, int BLOCK>
+constexpr int spw() {  // sample blocks per wave
+  return (K / 64 + BLOCK / 64 - 1) / (BLOCK / 64);
+}
+
+struct RowCtx {
+  int nv, lead, span, Q, q0, q1, qw0, nj, jf0, jf1;
+  int32_t* out;
+  int32_t* stats;
+  SlotFixed* sf;
+  SlotHeader* hdr;
+  uint32_t* slices;
+  uint2* s_pair;
+  const int32_t* hrow;
+};
+
+// Resolves row `slot` (part g) and issues its loads; false when the row is
+// finished already (a short row: identity written).  Split-tier hints write
+// the workgroup's LDS; the one-workgroup tier's loads touch no LDS.
 template <int K, int QPT, int BLOCK, bool SPLIT>
-__global__ void __launch_bounds__(BLOCK)
-    __attribute__((amdgpu_waves_per_eu(WavesPerEu<K, QPT, BLOCK, SPLIT>::value)))
-    gvr_topk_kernel(const GvrParams p) {
+__device__ __forceinline__ bool row_begin(const GvrParams& p, Smem<K, BLOCK>& sm, int slot, int g,
+                                          RowCtx& c, f4 (&v)[QPT],
+                                          float (&smp)[spw<K, BLOCK>()]) {
   constexpr int W = BLOCK / 64;           // waves
   constexpr int NSB = K / 64;             // sample blocks
   constexpr int SPW = (NSB + W - 1) / W;  // sample blocks per wave
-  constexpr int NW = (QPT * 4 + 31) / 32;
-  __shared__ Smem<K, BLOCK> sm;
-
   const int t = threadIdx.x;
   const int G = SPLIT ? p.wgs_per_row : 1;
-
-  // ---- workgroup -> (row slot, part) ------------------------------------
-  int slot, g;
-  if (SPLIT) {
-    int L = blockIdx.x;
-    if (p.xcd_group) {
-      // Workgroups are dispatched round-robin over the 8 XCDs; renumber so a
-      // row's G workgroups are consecutive within one XCD's sequence.
-      const int per = gridDim.x >> 3;
-      L = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
-    }
-    slot = L / G;
-    g = L - slot * G;
-  } else {
-    // Last row first: in a causal prefill tile a request's windows grow row
-    // by row, so its long rows start early and the launch drains on short
-    // ones (longest-first dispatch; decode batches of random lengths are
-    // indifferent to the order).  Measured on the 4096 x 16640 tile:
-    // 40.2 -> 38.2 us.
-    slot = (int)gridDim.x - 1 - (int)blockIdx.x;
-    g = 0;
-  }
-  if (slot >= p.rows) return;
   const int64_t row = (int64_t)p.row_begin + slot;
 
   // ---- row resolve (a0); row_stride < 2^30 is checked on the host --------
@@ -149,7 +148,7 @@ __global__ void __launch_bounds__(BLOCK)
     for (int i = g * BLOCK + t; i < K; i += G * BLOCK) store_nt(out + i, (i < nv) ? i : -1);
     if (stats && g == 0 && t < kStatsWords)
       stats[t] = (t == 0) ? 0 : (t == 6 ? G : (t == 7 ? p.cap : -1));
-    return;
+    return false;
   }
 
   // ---- part of the row this workgroup owns -------------------------------
@@ -187,7 +186,6 @@ __global__ void __launch_bounds__(BLOCK)
   // for nv > K, so the sample holds exactly K distinct scores, and the first
   // and last blocks touch both ends of the window.  Wave w reads blocks
   // w, w + W, ...: one 256-byte load per block.
-  float smp[SPW];
   {
     const float* win = rowp + ks;
     const SampleStep<NSB> ss(nv);
@@ -268,7 +266,6 @@ __global__ void __launch_bounds__(BLOCK)
   // fixed count of loads behind the sample's, the waits for the sample (and
   // for a group) are exact counts, so the bracket and, in the split tier,
   // the sample's floor run while the part is still in flight.
-  f4 v[QPT];
   {
     const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(base, q1 * 16);
     const int vo = (qw0 + l) * 16;
@@ -277,6 +274,52 @@ __global__ void __launch_bounds__(BLOCK)
       v[j] = __builtin_bit_cast(
           f4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, vo + j * BLOCK * 16, 0, kCachePolicyNT));
   }
+  c.nv = nv;
+  c.lead = lead;
+  c.span = span;
+  c.Q = Q;
+  c.q0 = q0;
+  c.q1 = q1;
+  c.qw0 = qw0;
+  c.nj = nj;
+  c.jf0 = jf0;
+  c.jf1 = jf1;
+  c.out = out;
+  c.stats = stats;
+  c.sf = sf;
+  c.hdr = hdr;
+  c.slices = slices;
+  c.s_pair = s_pair;
+  c.hrow = hrow;
+  return true;
+}
+
+// The selection of a row whose loads row_begin issued.
+template <int K, int QPT, int BLOCK, bool SPLIT>
+__device__ __forceinline__ void row_finish(const GvrParams& p, Smem<K, BLOCK>& sm, int g,
+                                           const RowCtx& c, f4 (&v)[QPT],
+                                           float (&smp)[spw<K, BLOCK>()]) {
+  constexpr int W = BLOCK / 64;           // waves
+  constexpr int NSB = K / 64;             // sample blocks
+  constexpr int SPW = (NSB + W - 1) / W;  // sample blocks per wave
+  constexpr int NW = (QPT * 4 + 31) / 32;
+  const int t = threadIdx.x;
+  const int G = SPLIT ? p.wgs_per_row : 1;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave index, uniform
+  const int l = lane_id();
+  const float qnan = __builtin_nanf("");
+  const int nv = c.nv, lead = c.lead, span = c.span, Q = c.Q, q0 = c.q0, q1 = c.q1;
+  const int qw0 = c.qw0, nj = c.nj, jf0 = c.jf0, jf1 = c.jf1;
+  int32_t* const out = c.out;
+  int32_t* const stats = c.stats;
+  SlotFixed* const sf = c.sf;
+  SlotHeader* const hdr = c.hdr;
+  uint32_t* const slices = c.slices;
+  uint2* const s_pair = c.s_pair;
+  const int32_t* const hrow = c.hrow;
+  (void)NSB;
+  (void)slices;
+  (void)s_pair;
   // Visit this thread's groups; `full` (uniform per wave) says all 64 lanes
   // hold four in-window scores, so only boundary waves pay for NaN checks.
   auto each = [&](auto&& f) {
@@ -325,7 +368,7 @@ __global__ void __launch_bounds__(BLOCK)
     sm.ctr[t] = 0u;
     sm.bc[t] = 0u;
   }
-  __syncthreads();
+  lds_sync();
   float gmin = sm.rmin[0], gmax = sm.rmax[0];
 #pragma unroll
   for (int i = 1; i < W; ++i) {
@@ -455,7 +498,7 @@ __global__ void __launch_bounds__(BLOCK)
             }
           });
         }
-        __syncthreads();
+        lds_sync();
         cr = crossing_1sync<BLOCK>(sm.u.hist, (uint32_t)K, sm.scan);
         path = (cr.b >= 0 && cr.m <= (uint32_t)one_wg_cap(K)) ? 1 : 3;
       };
@@ -478,7 +521,7 @@ __global__ void __launch_bounds__(BLOCK)
           const float e = bin_edge(kBins - 1, bm);
           if (l == 0) sm.thr[0] = e;
         }
-        __syncthreads();
+        lds_sync();
         float top = sm.hmax[0];
 #pragma unroll
         for (int i = 1; i < W; ++i) top = fmaxf(top, sm.hmax[i]);
@@ -491,7 +534,7 @@ __global__ void __launch_bounds__(BLOCK)
           bm = rm;
           xf = lo;
           for (int i = t; i < kBins + 64; i += BLOCK) sm.u.hist[i] = 0u;
-          __syncthreads();
+          lds_sync();
           verify(true);
           if (path == 1) path = 5;
         }
@@ -507,7 +550,7 @@ __global__ void __launch_bounds__(BLOCK)
         const float e = bin_edge(cr.b + w, bm);
         if (l == 0) sm.thr[w] = w == 0 ? fmaxf(e, xf) : e;
       }
-      __syncthreads();
+      lds_sync();
       const uint32_t need = (uint32_t)K - cr.above;
       uint32_t wb[NW];
 #pragma unroll
@@ -559,7 +602,7 @@ __global__ void __launch_bounds__(BLOCK)
           }
         }
       }
-      __syncthreads();
+      lds_sync();
       // ---- output (a9) and refine (a7) ------------------------------------
       // The winners staged by the walk go out with coalesced stores, and the
       // refine writes its `need` picks straight to the output: no barrier
@@ -586,7 +629,7 @@ __global__ void __launch_bounds__(BLOCK)
       } else {
         list_select<BLOCK>(sm.u.o.key, sm.u.o.idx, m, need, p.deterministic != 0, ob, cr.above,
                            (uint32_t)K, sm.dh, &sm.cross, sm.scan, sm.mm, sm.ctr, nbar);
-        __syncthreads();
+        lds_sync();
         put_rows(0u, (uint32_t)K);
       }
       put_stats(path, (int)cr.m, (int)cr.above, cr.b);
@@ -1042,6 +1085,42 @@ __global__ void __launch_bounds__(BLOCK)
       put_stats(path, bracket_ok && !SPLIT ? (int)cr.m : -1, bracket_ok && !SPLIT ? (int)cr.above : -1,
                 bracket_ok && !SPLIT ? cr.b : -1);
   }
+}
+
+template <int K, int QPT, int BLOCK, bool SPLIT>
+__global__ void __launch_bounds__(BLOCK)
+    __attribute__((amdgpu_waves_per_eu(WavesPerEu<K, QPT, BLOCK, SPLIT>::value)))
+    gvr_topk_kernel(const GvrParams p) {
+  __shared__ Smem<K, BLOCK> sm;
+  const int G = SPLIT ? p.wgs_per_row : 1;
+
+  // ---- workgroup -> (row slot, part) ------------------------------------
+  int slot, g;
+  if (SPLIT) {
+    int L = blockIdx.x;
+    if (p.xcd_group) {
+      // Workgroups are dispatched round-robin over the 8 XCDs; renumber so a
+      // row's G workgroups are consecutive within one XCD's sequence.
+      const int per = gridDim.x >> 3;
+      L = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+    }
+    slot = L / G;
+    g = L - slot * G;
+  } else {
+    // Last row first: in a causal prefill tile a request's windows grow row
+    // by row, so its long rows start early and the launch drains on short
+    // ones (longest-first dispatch; decode batches of random lengths are
+    // indifferent to the order).  Measured on the 4096 x 16640 tile:
+    // 40.2 -> 38.2 us.
+    slot = (int)gridDim.x - 1 - (int)blockIdx.x;
+    g = 0;
+  }
+  if (slot >= p.rows) return;
+  RowCtx c;
+  f4 v[QPT];
+  float smp[spw<K, BLOCK>()];
+  if (!row_begin<K, QPT, BLOCK, SPLIT>(p, sm, slot, g, c, v, smp)) return;
+  row_finish<K, QPT, BLOCK, SPLIT>(p, sm, g, c, v, smp);
 }
 
 // ---------------------------------------------------------------------------
