@@ -649,7 +649,7 @@ __device__ __forceinline__ void row_finish(const GvrParams& p, Smem<K, BLOCK>& s
         const float x = smp[i];
         lds_inc(hword(sm.u.hist, (x == x) ? vbin_off(x, bm) : 4u * (uint32_t)(kBins + l)));
       }
-      __syncthreads();
+      lds_sync();
       const float lam = (float)K * (float)K / (float)nv;
       const float rl = lam + 4.0f * sqrtf(lam) + 8.0f;
       const uint32_t rlow = rl >= (float)K ? (uint32_t)K : (uint32_t)rl;
@@ -684,7 +684,7 @@ __device__ __forceinline__ void row_finish(const GvrParams& p, Smem<K, BLOCK>& s
       // can share a bin on a smooth stretch of the row without the row being
       // crowded.
       const float crowded = fmaxf(2.0f * (float)kSingleCap * (float)K / (float)nv, 32.0f);
-      __syncthreads();  // every wave has read the sample's counts
+      lds_sync();  // every wave has read the sample's counts
       {
         // four bins per read; each thread then clears what it read
         uint32_t mx = 0u;
@@ -703,7 +703,7 @@ __device__ __forceinline__ void row_finish(const GvrParams& p, Smem<K, BLOCK>& s
         if (mx >= 8u) sm.bc[3] = 1u;
         if ((float)mx >= crowded) sm.ctr[3] = 1u;
       }
-      __syncthreads();
+      lds_sync();
       path = sm.ctr[3] ? 3 : 1;
     }
     mark_ends();
@@ -727,7 +727,7 @@ __device__ __forceinline__ void row_finish(const GvrParams& p, Smem<K, BLOCK>& s
         const float e = bin_edge(bl, bm);
         if (l == 0) sm.thr[0] = e;
       }
-      __syncthreads();
+      lds_sync();
       const float xf = fmaxf(sm.thr[0], xfloor);
       if (sm.bc[3]) {
         each([&](int j, int q, bool) {
@@ -753,7 +753,7 @@ __device__ __forceinline__ void row_finish(const GvrParams& p, Smem<K, BLOCK>& s
             if (b[e] >= 0) lds_inc(hword(sm.u.hist, (uint32_t)b[e]));
         });
       }
-      __syncthreads();
+      lds_sync();
       {
         constexpr int PER = kBins / BLOCK;
         const int hi = kBins - 1 - t * PER;
@@ -789,7 +789,7 @@ __device__ __forceinline__ void row_finish(const GvrParams& p, Smem<K, BLOCK>& s
 #pragma unroll
         for (int i = 0; i < BPT; ++i) sm.u.hist[t + i * BLOCK] = r[i];
       }
-      __syncthreads();
+      lds_sync();
       // ---- crossing bin (a5), the same in every workgroup of the row -----
       cr = crossing_1sync<BLOCK>(sm.u.hist, (uint32_t)K, sm.scan);
       // Merged counts below K (the sample's floor lay above the K-th value)
@@ -823,7 +823,7 @@ __device__ __forceinline__ void row_finish(const GvrParams& p, Smem<K, BLOCK>& s
           const float e = bin_edge(kBins - 1, bm);
           if (l == 0) sm.thr[0] = e;
         }
-        __syncthreads();
+        lds_sync();
         if (t == 0) {
           float pm = sm.hmax[0];
           for (int i = 1; i < W; ++i) pm = fmaxf(pm, sm.hmax[i]);
@@ -845,7 +845,7 @@ __device__ __forceinline__ void row_finish(const GvrParams& p, Smem<K, BLOCK>& s
         }
       }
       if (retry) {
-        __syncthreads();  // every wave has read the merged counts
+        lds_sync();  // every wave has read the merged counts
         for (int i = t; i < kBins + 64; i += BLOCK) sm.u.hist[i] = 0u;
         floor_bin = 0;
         path = verify(0, &sf->dig[0][0]);
@@ -886,7 +886,7 @@ __device__ __forceinline__ void row_finish(const GvrParams& p, Smem<K, BLOCK>& s
           sm.bc[1] = om;
         }
       }
-      __syncthreads();
+      lds_sync();
       const uint32_t need = (uint32_t)K - cr.above;
       const uint32_t m = cr.m;
       const uint32_t above = cr.above;
@@ -984,7 +984,7 @@ __device__ __forceinline__ void row_finish(const GvrParams& p, Smem<K, BLOCK>& s
             }
           }
         }
-        __syncthreads();
+        lds_sync();
         if (m <= (uint32_t)kRankMax) {
           rank_select_direct<BLOCK>(sm.u.c.key, sm.u.c.idx, m, need, out, above);
         } else {
@@ -1053,7 +1053,7 @@ __device__ __forceinline__ void row_finish(const GvrParams& p, Smem<K, BLOCK>& s
         sm.bc[0] = atomic_add_agent(&hdr->win_cur, tot & 0xFFFFu);
         sm.bc[1] = atomic_add_agent(&hdr->tie_cur, tot >> 16);
       }
-      __syncthreads();
+      lds_sync();
       gbase = sm.bc[0];
       ebase = sm.bc[1];
     }
