@@ -432,15 +432,29 @@ __device__ __forceinline__ void row_finish(const GvrParams& p, Smem<K, BLOCK>& s
       const int lt = tl & 63;
       const int tail = q1 == Q ? span - ((Q - 1) << 2) : 4;  // scores of the last group, 1..4
       if (w == (tl >> 6) && (lt < 63 || tail < 4)) {
+        if constexpr (QPT <= 4) {
+          // (selects on every group: with so few groups the compiler turns
+          // the branch form below into one store at a computed index, which
+          // moves the row's registers to scratch memory)
 #pragma unroll
-        for (int j = 0; j < QPT; ++j)
-          if (j == jl) {
+          for (int j = 0; j < QPT; ++j) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const bool keep = l < lt || (l == lt && e < tail);
+              const bool keep = j != jl || l < lt || (l == lt && e < tail);
               v[j][e] = keep ? v[j][e] : qnan;
             }
           }
+        } else {
+#pragma unroll
+          for (int j = 0; j < QPT; ++j)
+            if (j == jl) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const bool keep = l < lt || (l == lt && e < tail);
+                v[j][e] = keep ? v[j][e] : qnan;
+              }
+            }
+        }
       }
     }
   };
@@ -485,18 +499,32 @@ __device__ __forceinline__ void row_finish(const GvrParams& p, Smem<K, BLOCK>& s
               if (b[e] >= 0) lds_inc(hword(sm.u.hist, (uint32_t)b[e]));
           });
         } else {
-          each([&](int j, int q, bool full) {
-            if (full) {
+          // Every visited score is counted, the NaN markers with the rest:
+          // they all land in the one bin a NaN maps to, and each wave takes
+          // its markers out of it below (no per-group test, no per-score
+          // NaN check).
+          each([&](int j, int q, bool) {
 #pragma unroll
-              for (int e = 0; e < 4; ++e) lds_inc(hword(sm.u.hist, vbin_off(v[j][e], bm)));
-            } else {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const float x = v[j][e];
-                lds_inc(hword(sm.u.hist, (x == x) ? vbin_off(x, bm) : 4u * (uint32_t)(kBins + l)));
-              }
-            }
+            for (int e = 0; e < 4; ++e) lds_inc(hword(sm.u.hist, vbin_off(v[j][e], bm)));
           });
+          // The wave's markers: its visited groups hold 256 scores each
+          // (window positions 4 qw0 + 1024 j - lead onwards); only the first
+          // (the window's lead) and the last (the window's end) can reach
+          // outside [0, nv).
+          int njp = nj;
+          asm volatile("" : "+s"(njp));
+          if (l == 0 && njp > 0) {
+            auto inwin = [&](int j) {  // in-window scores of the wave's group j
+              const int st = 4 * (qw0 + j * BLOCK) - lead;
+              const int lo = st > 0 ? st : 0;
+              const int hi = st + 256 < nv ? st + 256 : nv;
+              return hi > lo ? hi - lo : 0;
+            };
+            const int inside = njp == 1 ? inwin(0) : inwin(0) + 256 * (njp - 2) + inwin(njp - 1);
+            const uint32_t mk = (uint32_t)(256 * njp - inside);
+            if (mk) (void)__hip_atomic_fetch_sub(hword(sm.u.hist, vbin_off(qnan, bm)), mk,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          }
         }
         lds_sync();
         cr = crossing_1sync<BLOCK>(sm.u.hist, (uint32_t)K, sm.scan);
