@@ -53,7 +53,7 @@ struct alignas(16) BskSmem {
   uint32_t list[kBskCap];     // survivor block ids
   uint32_t key[kBskMembers];
   int32_t idx[kBskMembers];
-  uint32_t dh[256];
+  alignas(16) uint32_t dh[256];  // radix digit counts (cleared as 16-byte words)
   uint32_t mm[2 * (kBskBlock / 64)];  // per-wave class extremes of a radix level
   uint32_t scan[kBskBlock / 64];
   float rmin[kBskBlock / 64];

@@ -40,6 +40,9 @@ __device__ __forceinline__ uint32_t rkey(float x) { return (x == x) ? fkey(x) : 
 constexpr int kBufWord3 = 0x00020000;
 // Cache policy of streaming loads: non-temporal (the scores are read once).
 constexpr int kCachePolicyNT = 2;
+// Cache policy of loads of what other workgroups wrote by agent-scope
+// atomics: sc1, as on the compiler's own agent-scope atomic loads.
+constexpr int kCachePolicyAgent = 16;
 
 // Raw buffer resource over [p, p + bytes) (p and bytes uniform: both go
 // through readfirstlane so the descriptor lives in scalar registers).
@@ -468,24 +471,19 @@ __device__ __forceinline__ Cross read_cross(const Cross* c) {
   return r;
 }
 
-// Find the highest bin b with sum_{b' >= b} h[b'] >= target over NBINS bins,
-// where load(b) returns h[b].  Thread t owns PER consecutive bins from the
-// top.  Result in *out (LDS), visible to all threads on return.
-template <int NBINS, int BLOCK, class Load>
-__device__ __forceinline__ void find_crossing(Load&& load, uint32_t target, Cross* out,
+// The crossing from counts already in registers: thread t holds c[i] =
+// h[NBINS - 1 - t * PER - i] (PER consecutive bins from the top; threads
+// past NBINS / PER hold zeros).  Result in *out (LDS), visible to all threads
+// on return.
+template <int NBINS, int BLOCK, int PER>
+__device__ __forceinline__ void crossing_from(const uint32_t (&c)[PER], uint32_t target, Cross* out,
                                               uint32_t* scan_sm) {
-  constexpr int PER = NBINS >= BLOCK ? NBINS / BLOCK : 1;
   constexpr int OWNERS = NBINS / PER;
-  static_assert(PER * OWNERS == NBINS, "bins per thread");
   const int t = threadIdx.x;
   const int hi = NBINS - 1 - t * PER;
-  uint32_t c[PER];
   uint32_t s = 0;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    c[i] = (t < OWNERS) ? load(hi - i) : 0u;
-    s += c[i];
-  }
+  for (int i = 0; i < PER; ++i) s += c[i];
   uint32_t tot;
   const uint32_t ex = block_excl_scan<BLOCK>(s, scan_sm, tot);
   if (t < OWNERS && ex < target && ex + s >= target) {
@@ -510,6 +508,49 @@ __device__ __forceinline__ void find_crossing(Load&& load, uint32_t target, Cros
     out->total = tot;
   }
   lds_sync();
+}
+
+// Find the highest bin b with sum_{b' >= b} h[b'] >= target over NBINS bins,
+// where load(b) returns h[b].  Thread t owns PER consecutive bins from the
+// top.  Result in *out (LDS), visible to all threads on return.
+template <int NBINS, int BLOCK, class Load>
+__device__ __forceinline__ void find_crossing(Load&& load, uint32_t target, Cross* out,
+                                              uint32_t* scan_sm) {
+  constexpr int PER = NBINS >= BLOCK ? NBINS / BLOCK : 1;
+  constexpr int OWNERS = NBINS / PER;
+  static_assert(PER * OWNERS == NBINS, "bins per thread");
+  const int t = threadIdx.x;
+  const int hi = NBINS - 1 - t * PER;
+  uint32_t c[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) c[i] = (t < OWNERS) ? load(hi - i) : 0u;
+  crossing_from<NBINS, BLOCK, PER>(c, target, out, scan_sm);
+}
+
+// find_crossing over NBINS counts in global memory that other workgroups
+// merged by agent-scope atomics (complete before the caller's row barrier):
+// each thread reads its PER consecutive bins as 16-byte loads with the
+// agent-coherent cache policy (the one the compiler gives agent-scope atomic
+// loads), so a wave's load covers one contiguous stretch.
+template <int NBINS, int BLOCK>
+__device__ __forceinline__ void find_crossing_agent(const uint32_t* h, uint32_t target, Cross* out,
+                                                    uint32_t* scan_sm) {
+  constexpr int PER = NBINS / BLOCK;
+  static_assert(PER % 4 == 0 && PER * BLOCK == NBINS, "whole 16-byte groups per thread");
+  const int t = threadIdx.x;
+  const int lo = NBINS - (t + 1) * PER;  // this thread's lowest bin
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(h, NBINS * 4);
+  uint32_t c[PER];
+#pragma unroll
+  for (int v = 0; v < PER / 4; ++v) {
+    const uint4 q = __builtin_bit_cast(
+        uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, (lo + 4 * v) * 4, 0, kCachePolicyAgent));
+    c[PER - 1 - 4 * v] = q.x;
+    c[PER - 2 - 4 * v] = q.y;
+    c[PER - 3 - 4 * v] = q.z;
+    c[PER - 4 - 4 * v] = q.w;
+  }
+  crossing_from<NBINS, BLOCK, PER>(c, target, out, scan_sm);
 }
 
 // The crossing over the kBins-word LDS histogram h with a single workgroup
@@ -672,13 +713,16 @@ __device__ __forceinline__ bool finish_slot(SlotHeader* hdr, int G, uint32_t* bc
 }
 
 // Return a row's slot to its resting state (all zero): the histogram from bin
-// hist_lo up (no round adds below its floor), the digit rows when `dig`, and
-// the header.
-__device__ __forceinline__ void rest_slot(SlotFixed* sf, int t, int block, int hist_lo, bool dig) {
-  if (dig) {
-    for (int i = t; i < 8 * 256; i += block) (&sf->dig[0][0])[i] = 0u;
-    if (t < 16) sf->hdr.class_ext[t] = 0u;
-  }
+// hist_lo up (no round adds below its floor), the first `rrows` rescue digit
+// rows and the first `trows` tie-pick rows (with any of them, the class
+// extremes too), and the header.
+__device__ __forceinline__ void rest_slot(SlotFixed* sf, int t, int block, int hist_lo, int rrows,
+                                          int trows) {
+  for (int i = t; i < rrows * kRescueDigitBins / 4; i += block)
+    reinterpret_cast<uint4*>(&sf->rdig[0][0])[i] = uint4{0u, 0u, 0u, 0u};
+  for (int i = t; i < trows * 256 / 4; i += block)
+    reinterpret_cast<uint4*>(&sf->tdig[0][0])[i] = uint4{0u, 0u, 0u, 0u};
+  if (rrows + trows > 0 && t < 16) sf->hdr.class_ext[t] = 0u;
   for (int i = hist_lo + t; i < kBins; i += block) sf->hist[i] = 0u;
   if (t == 0) {
     sf->hdr.bar_count = 0u;
@@ -695,45 +739,59 @@ __device__ __forceinline__ void rest_slot(SlotFixed* sf, int t, int block, int h
 
 struct RSel {
   uint32_t thr;    // key >> shift of the threshold digit path
-  int shift;       // 24, 16, 8 or 0
+  int shift;       // the lowest bit of the fixed digits (0 for a whole key)
   uint32_t rem;    // how many of the elements with key >> shift == thr to take
   uint32_t cnt;    // how many elements have key >> shift == thr
+  int levels;      // digit levels counted
 };
 
 // The `need` largest keys among the elements `iter` visits (iter(f) calls
-// f(key) for each element this thread owns): up to four 8-bit digit levels
-// from the top, stopping early when the crossing digit's members are all
-// needed.  Afterwards an element is selected iff key >> shift > thr, or
-// key >> shift == thr and it is one of `rem` such elements.  With `gdig`
-// (split rescue) the digit counts of the row's G workgroups are summed
-// through the workspace behind a barrier at each level.  Each level also
-// finds the extremes of the class it counts (the keys that share the digits
-// fixed so far), through `mm` (2 * BLOCK / 64 LDS words) and, split, the
-// eight `gext` words (atomic max, zero at rest): a class holding a single key
-// (all-equal rows, the ties of a two-valued row, a zero class) ends the
-// selection with that key at once instead of after all four levels.  With
-// EXT false (callers short of VGPRs) the extremes are not tracked.
-template <int BLOCK, bool AGG = false, bool EXT = false, class Iter>
+// f(key) for each element this thread owns): digit levels of DB bits from the
+// top (the last level takes what is left of the 32 bits: 8-bit digits give
+// four levels, 11-bit ones three of 11, 11 and 10 bits), stopping early when
+// the crossing digit's members are all needed.  Afterwards an element is
+// selected iff key >> shift > thr, or key >> shift == thr and it is one of
+// `rem` such elements.  `dh` holds 2^DB LDS words.  With `gdig` (split
+// rescue) the digit counts of the row's G workgroups are summed through the
+// workspace (one row of 2^DB words per level) behind a barrier at each
+// level.  Each level also finds the extremes of the class it counts (the
+// keys that share the digits fixed so far), through `mm` (2 * BLOCK / 64 LDS
+// words) and, split, the eight `gext` words (atomic max, zero at rest): a
+// class holding a single key (all-equal rows, the ties of a two-valued row, a
+// zero class) ends the selection with that key at once instead of after every
+// level.  With EXT false (callers short of VGPRs) the extremes are not
+// tracked.
+template <int BLOCK, bool AGG = false, bool EXT = false, int DB = 8, class Iter>
 __device__ __forceinline__ RSel radix_select(Iter&& iter, uint32_t need, uint32_t* dh, Cross* cross,
                                              uint32_t* scan, uint32_t* mm, uint32_t* gdig,
                                              uint32_t* gext, SlotHeader* hdr, int G,
                                              uint32_t& nbar, const BarrierSync& sy) {
   constexpr int W = BLOCK / 64;
+  constexpr int NB = 1 << DB;
+  constexpr int NL = (32 + DB - 1) / DB;
+  static_assert(NL <= 4, "class extremes are kept for four levels");
   const int t = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   uint32_t prefix = 0, rem = need, cnt = 0;
-  int shift = 24;
-  for (int L = 0; L < 4; ++L) {
-    shift = 24 - 8 * L;
-    for (int i = t; i < 256; i += BLOCK) dh[i] = 0u;
+  int shift = 32, L = 0;
+  while (L < NL) {
+    const int hs = shift;  // the digits from bit hs up are fixed
+    shift = 32 - DB * (L + 1) > 0 ? 32 - DB * (L + 1) : 0;
+    const uint32_t dmask = (2u << (hs - shift - 1)) - 1u;
+    if constexpr (NB >= 4 * BLOCK) {
+      for (int i = t; i < NB / 4; i += BLOCK) reinterpret_cast<uint4*>(dh)[i] = uint4{0u, 0u, 0u, 0u};
+    } else {
+      for (int i = t; i < NB; i += BLOCK) dh[i] = 0u;
+    }
     lds_sync();
     uint32_t kmax = 0u, knmin = 0u;  // the class's largest key, smallest complemented
     iter([&](uint32_t key) {
-      const bool act = L == 0 || ((key ^ prefix) >> (shift + 8)) == 0u;
+      const bool act = L == 0 || ((key ^ prefix) >> hs) == 0u;
+      const uint32_t d = (key >> shift) & dmask;
       if (AGG)
-        lds_inc_agg(dh, (key >> shift) & 255u, act);
+        lds_inc_agg(dh, d, act);
       else if (act)
-        lds_inc(&dh[(key >> shift) & 255u]);
+        lds_inc(&dh[d]);
       if (EXT && act) {
         kmax = max(kmax, key);
         knmin = max(knmin, ~key);
@@ -755,10 +813,10 @@ __device__ __forceinline__ RSel radix_select(Iter&& iter, uint32_t need, uint32_
       }
     }
     if (gdig) {
-      uint32_t* gd = gdig + L * 256;
-      for (int i = t; i < 256; i += BLOCK) {
+      uint32_t* gd = gdig + L * NB;
+      for (int i = t; i < NB; i += BLOCK) {
         const uint32_t c = dh[i];
-        if (c) atomic_add_agent(&gd[i], c);
+        if (c) atomic_add_agent_nr(&gd[i], c);
       }
       if (EXT && t == 0) {
         if (kmax) __hip_atomic_fetch_max(&gext[L], kmax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -766,14 +824,25 @@ __device__ __forceinline__ RSel radix_select(Iter&& iter, uint32_t need, uint32_
           __hip_atomic_fetch_max(&gext[4 + L], knmin, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       row_barrier(hdr, G, nbar, sy);
-      find_crossing<256, BLOCK>([&](int d) { return load_agent(&gd[d]); }, rem, cross, scan);
+      // the merged extremes are loaded first, so that their round trip is
+      // the counts' own
+      uint32_t gmx = 0u, gmn = 0u;
       if (EXT) {
-        kmax = (uint32_t)__builtin_amdgcn_readfirstlane((int)load_agent(&gext[L]));
-        knmin = (uint32_t)__builtin_amdgcn_readfirstlane((int)load_agent(&gext[4 + L]));
+        gmx = load_agent(&gext[L]);
+        gmn = load_agent(&gext[4 + L]);
+      }
+      if constexpr (NB >= 4 * BLOCK)
+        find_crossing_agent<NB, BLOCK>(gd, rem, cross, scan);
+      else
+        find_crossing<NB, BLOCK>([&](int d) { return load_agent(&gd[d]); }, rem, cross, scan);
+      if (EXT) {
+        kmax = (uint32_t)__builtin_amdgcn_readfirstlane((int)gmx);
+        knmin = (uint32_t)__builtin_amdgcn_readfirstlane((int)gmn);
       }
     } else {
-      find_crossing<256, BLOCK>([&](int d) { return dh[d]; }, rem, cross, scan);
+      find_crossing<NB, BLOCK>([&](int d) { return dh[d]; }, rem, cross, scan);
     }
+    ++L;
     const Cross c = read_cross(cross);
     prefix |= (uint32_t)c.b << shift;
     rem -= c.above;
@@ -787,7 +856,7 @@ __device__ __forceinline__ RSel radix_select(Iter&& iter, uint32_t need, uint32_
       break;
     }
   }
-  return RSel{prefix >> shift, shift, rem, cnt};
+  return RSel{prefix >> shift, shift, rem, cnt, L};
 }
 
 // The `need` largest of the m (key, index) pairs held in LDS, written from
