@@ -784,6 +784,10 @@ __device__ __forceinline__ void row_finish(const GvrParams& p, Smem<K, BLOCK>& s
       }
       lds_sync();
       {
+        // suffix counts: thread t owns PER consecutive bins from the top and
+        // writes them as 16-byte words (whole lines per wave) with the
+        // agent-coherent cache policy; groups wholly below the floor are
+        // skipped (nothing reads a slice below the crossing bin)
         constexpr int PER = kBins / BLOCK;
         const int hi = kBins - 1 - t * PER;
         uint32_t c[PER];
@@ -795,15 +799,35 @@ __device__ __forceinline__ void row_finish(const GvrParams& p, Smem<K, BLOCK>& s
         }
         uint32_t tot;
         uint32_t run = block_excl_scan<BLOCK>(sum, sm.scan, tot);
-        uint32_t* mine = slices + (size_t)g * kBins;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(slices + (size_t)g * kBins, kBins * 4);
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-          const int b = hi - i;
           run += c[i];
-          if (b >= bl) {
-            __hip_atomic_store(&mine[b], run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (c[i]) atomic_add_agent_nr(&gh[b], c[i]);
+          c[i] = run;
+        }
+        if constexpr (PER % 4 == 0) {
+#pragma unroll
+          for (int q4 = 0; q4 < PER / 4; ++q4) {
+            const int b0 = hi - PER + 1 + 4 * q4;  // the group's lowest bin
+            if (b0 + 3 >= bl) {
+              typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+              const v4u sv = {c[PER - 1 - 4 * q4], c[PER - 2 - 4 * q4], c[PER - 3 - 4 * q4],
+                              c[PER - 4 - 4 * q4]};
+              __builtin_amdgcn_raw_buffer_store_b128(sv, rs, b0 * 4, 0, kCachePolicyAgent);
+            }
           }
+        } else {
+          // (no split part runs more than 512 threads)
+          uint32_t* mine = slices + (size_t)g * kBins;
+#pragma unroll
+          for (int i = 0; i < PER; ++i)
+            if (hi - i >= bl)
+              __hip_atomic_store(&mine[hi - i], c[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        // the row's histogram: one bin per lane, consecutive across a wave
+        for (int b = t; b < kBins; b += BLOCK) {
+          const uint32_t n = b >= bl ? sm.u.hist[b] : 0u;
+          if (n) atomic_add_agent_nr(&gh[b], n);
         }
       }
       row_barrier(hdr, G, nbar, p.sync);

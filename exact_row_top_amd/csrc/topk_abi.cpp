@@ -418,6 +418,7 @@ int run(int mode, const float* logits, int64_t row_stride, const int32_t* e1, co
   unsigned char* ws = nullptr;
   if (pl.G > 1) {
     if (workspace) {
+      if (!aligned(workspace, 16)) return TOPK_ELAYOUT;
       if (workspace_bytes < pl.ws_bytes) return TOPK_EWORKSPACE;
       ws = static_cast<unsigned char*>(workspace);
     } else {
@@ -663,7 +664,7 @@ const char* topk_strerror(int status) {
   switch (status) {
     case TOPK_OK: return "ok";
     case TOPK_EINVAL: return "invalid argument (null pointer, num_rows < 0, k not in {512,1024,2048}, row_stride < 1, or row too long)";
-    case TOPK_ELAYOUT: return "unsupported layout (logits must be 16-byte aligned with row_stride % 4 == 0; indices/extents 4-byte aligned)";
+    case TOPK_ELAYOUT: return "unsupported layout (logits and workspace must be 16-byte aligned with row_stride % 4 == 0; indices/extents 4-byte aligned)";
     case TOPK_EWORKSPACE: return "workspace smaller than topk_workspace_bytes()";
     case TOPK_EDEVICE: return "current device is not gfx950";
     case TOPK_ELAUNCH: return "HIP launch or allocation failed";
@@ -782,6 +783,7 @@ int topk_validate(int32_t mode, const void* logits, int64_t row_stride, const vo
     Plan pl;
     rc = make_plan(num_rows, env, k, 0, (int64_t)1 << 40, &pl);
     if (rc != TOPK_OK) return rc;
+    if (pl.G > 1 && !aligned(workspace, 16)) return TOPK_ELAYOUT;
     if (pl.G > 1 && workspace_bytes < ws_bytes_upper(num_rows, env, k, 0)) return TOPK_EWORKSPACE;
   }
   return TOPK_OK;

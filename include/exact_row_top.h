@@ -45,7 +45,9 @@
  *    written for it are unspecified: they need not be distinct, nor inside
  *    the window.  +-inf are ordinary values; -0 and +0 are equal.
  *  - workspace: optional caller-owned device buffer of at least
- *    topk_workspace_bytes(...) bytes, zeroed ONCE by topk_workspace_init before
+ *    topk_workspace_bytes(...) bytes, 16-byte aligned (TOPK_ELAYOUT
+ *    otherwise: the split tier moves its counts as 16-byte words), zeroed
+ *    ONCE by topk_workspace_init before
  *    its first use; every call returns it to that resting state (histograms,
  *    cursors and counters back to zero), so a captured graph can replay
  *    without a memset.  The
@@ -88,7 +90,8 @@ enum {
                           1,179,648 scores from the 16-byte boundary below
                           the window's start) */
   TOPK_ELAYOUT = 2,    /* logits not 16-byte aligned, row_stride % 4 != 0,
-                          indices / extents not 4-byte aligned */
+                          indices / extents not 4-byte aligned, a caller
+                          workspace the plan uses not 16-byte aligned */
   TOPK_EWORKSPACE = 3, /* caller workspace smaller than topk_workspace_bytes
                           (topk_decode_noalloc: a plan larger than its fixed
                           scratch) */

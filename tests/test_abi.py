@@ -91,6 +91,10 @@ def test_validate_workspace_size():
     assert need > 0
     assert _validate(stride=131072, rows=64, k=2048, ws=P16, ws_bytes=need) == 0
     assert _validate(stride=131072, rows=64, k=2048, ws=P16, ws_bytes=need - 1) == ert.TOPK_EWORKSPACE
+    # the split tier moves its counts as 16-byte words
+    assert _validate(stride=131072, rows=64, k=2048, ws=P16 + 8, ws_bytes=need) == ert.TOPK_ELAYOUT
+    # a plan without the split tier takes no workspace, aligned or not
+    assert _validate(stride=4096, rows=4096, k=512, ws=P16 + 8, ws_bytes=need) == 0
 
 
 def test_workspace_layout():
