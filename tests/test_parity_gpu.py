@@ -315,6 +315,35 @@ def test_caller_workspace_matches_and_returns_to_rest(ert):
     assert np.all(blocks == 0), "slot blocks not at rest"
 
 
+def test_workspace_rests_after_every_rescue_level(ert):
+    # The tie-heavy batch takes the split rescue on every row: the 40000
+    # distinct scores in one value bin need all three digit levels, the
+    # deterministic tie pick adds its own levels; the row's last workgroup
+    # must clear exactly the digit rows those levels used.
+    import torch
+    w = workloads.tie_heavy()
+    want = oracle.topk_workload(w)
+    ws = ert.new_workspace(w.num_rows, w.row_stride, w.k)
+    assert ws is not None
+    dev = to_dev(w)
+    lay = ert.workspace_layout()
+    h, f, n = lay["header_bytes"] // 4, lay["slot_fixed_bytes"] // 4, lay["slots"]
+    for kw in ({}, {"deterministic": True, "sorted": True}, {"force_rescue": True},
+               {"force_rescue": True, "deterministic": True, "sorted": True}):
+        log(f"[rest] tie_heavy {kw}")
+        out = ert.topk_decode(dev["logits"], dev["n_valid"], w.k, workspace=ws, **kw)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        if kw.get("deterministic"):
+            bad = [r for r in range(w.num_rows) if not np.array_equal(got[r], want[r])]
+            assert not bad, f"{kw}: rows {bad} differ from the canonical output"
+        else:
+            assert_parity(w, got, want)
+        words = ws.view(torch.int32).cpu().numpy()
+        assert np.all(words[:h] == 0), kw
+        assert np.all(words[h:h + n * f] == 0), f"{kw}: slot blocks not at rest"
+
+
 def test_repeat_runs_are_stable(ert):
     w = workloads.decode_varlen(rows=8)
     dev = to_dev(w)
