@@ -48,6 +48,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "gvr_common.h"
 #include "gvr_device.h"
 #include "row_window.h"
@@ -296,6 +298,18 @@ __device__ __forceinline__ bool row_begin(const GvrParams& p, Smem<K, BLOCK>& sm
 }
 
 // The selection of a row whose loads row_begin issued.
+// Visit groups J, J + 1, ... while they are below n (uniform): the tests
+// nest, so the first group past n ends the visit with one branch.
+template <int J, int N, class G>
+__device__ __forceinline__ void visit_groups(int n, G&& g) {
+  if constexpr (J < N) {
+    if (J < n) {
+      g(std::integral_constant<int, J>{});
+      visit_groups<J + 1, N>(n, g);
+    }
+  }
+}
+
 template <int K, int QPT, int BLOCK, bool SPLIT>
 __device__ __forceinline__ void row_finish(const GvrParams& p, Smem<K, BLOCK>& sm, int g,
                                            const RowCtx& c, f4 (&v)[QPT],
@@ -330,14 +344,12 @@ __device__ __forceinline__ void row_finish(const GvrParams& p, Smem<K, BLOCK>& s
     int ll = l, njp = nj, jf0p = jf0, jf1p = jf1;
     asm volatile("" : "+v"(ll));
     asm volatile("" : "+s"(njp));
-#pragma unroll
-    for (int j = 0; j < QPT; ++j) {
-      if (j < njp) {
-        const int q = qw0 + j * BLOCK + ll;
-        const bool full = j >= jf0p && j < jf1p;
-        f(j, q, full);
-      }
-    }
+    visit_groups<0, QPT>(njp, [&](auto J) {
+      constexpr int j = decltype(J)::value;
+      const int q = qw0 + j * BLOCK + ll;
+      const bool full = j >= jf0p && j < jf1p;
+      f(j, q, full);
+    });
   };
   auto resident = [&](auto&& f) {
     each([&](int j, int q, bool) {
