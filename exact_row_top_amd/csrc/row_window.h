@@ -16,11 +16,19 @@ __device__ __forceinline__ void row_window(const int32_t* n_valid, const int32_t
                                            const int32_t* row_ends, const VarlenForm& vf,
                                            int64_t row, int S, int* ks, int* nv) {
   if (vf.kv_lens) {
-    const int64_t kv = vf.kv_lens[row / vf.next_n];
-    const int64_t t = kv - vf.next_n + (row % vf.next_n) + 1;
-    const int64_t n = kv < vf.next_n ? 0 : t / vf.compress_ratio;
+    // row < 2^31 and next_n, compress_ratio >= 1 (checked on the host): the
+    // quotients are 32-bit unsigned ones; with kv >= next_n the numerator
+    // kv - next_n + row % next_n + 1 lies in [1, kv]
+    const uint32_t r = (uint32_t)row, nn = (uint32_t)vf.next_n;
+    const uint32_t req = r / nn;
+    const int32_t kv = vf.kv_lens[req];
+    int n = 0;
+    if (kv >= vf.next_n) {
+      const uint32_t t = (uint32_t)(kv - vf.next_n) + (r - req * nn) + 1u;
+      n = (int)(t / (uint32_t)vf.compress_ratio);
+    }
     *ks = 0;
-    *nv = n < 0 ? 0 : (n > S ? S : (int)n);
+    *nv = n > S ? S : n;
   } else if (n_valid) {
     const int n = n_valid[row];
     *ks = 0;
