@@ -297,7 +297,6 @@ __device__ __forceinline__ bool row_begin(const GvrParams& p, Smem<K, BLOCK>& sm
   return true;
 }
 
-// The selection of a row whose loads row_begin issued.
 // Visit groups J, J + 1, ... while they are below n (uniform): the tests
 // nest, so the first group past n ends the visit with one branch.
 template <int J, int N, class G>
@@ -310,6 +309,7 @@ __device__ __forceinline__ void visit_groups(int n, G&& g) {
   }
 }
 
+// The selection of a row whose loads row_begin issued.
 template <int K, int QPT, int BLOCK, bool SPLIT>
 __device__ __forceinline__ void row_finish(const GvrParams& p, Smem<K, BLOCK>& sm, int g,
                                            const RowCtx& c, f4 (&v)[QPT],
@@ -917,8 +917,8 @@ __device__ __forceinline__ void row_finish(const GvrParams& p, Smem<K, BLOCK>& s
         if (path == 1) {
           path = 5;
         } else {
-          // the rescue merges its digit counts in those rows: every
-          // workgroup has read them; back to zero, then on
+          // the rescue merges its first level's digit counts in that row:
+          // every workgroup has read it; back to zero, then on
           row_barrier(hdr, G, nbar, p.sync);
           for (int i = t; i < kRescueDigitBins; i += BLOCK)
             __hip_atomic_store(&sf->rdig[0][0] + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1058,7 +1058,7 @@ __device__ __forceinline__ void row_finish(const GvrParams& p, Smem<K, BLOCK>& s
         }
       }
       // back to zero: the histogram bins the first round added to, and the
-      // digit rows when a second round used them
+      // first digit row when a second round used it
       rest_slot(sf, t, BLOCK, blo, path == 5 ? 1 : 0, 0);
       put_stats(path, (int)cr.m, (int)cr.above, cr.b);
       return;
