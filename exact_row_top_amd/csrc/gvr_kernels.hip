@@ -1007,11 +1007,17 @@ __device__ __forceinline__ void row_finish(const GvrParams& p, Smem<K, BLOCK>& s
           }
         });
       }
-      // ---- refine (a7): the row's last workgroup picks `need` members -----
-      // The done count waits for the member list only: the winners go out
-      // after it (nothing reads them in this launch), so their stores overlap
-      // its round trip and the last workgroup's refine.
-      const bool last = finish_slot(hdr, G, &sm.bc[2]);
+      // ---- refine (a7): the row's last part picks `need` members ----------
+      // Every workgroup counts itself done once its member-list entries have
+      // completed (an add without return: a returning one's round trip is
+      // the longer), then writes its winners (nothing reads them in this
+      // launch, so their stores overlap the count's round trip).  The row's
+      // last part waits for the count to reach G -- a bounded wait, like
+      // the row barrier's -- and refines.
+      wait_vm();
+      __syncthreads();
+      if (t == 0) atomic_add_agent_nr(&hdr->done, 1u);
+      const bool last = g == G - 1;
       {
         uint32_t wpos = sm.bc[0] + (ex & 0xFFFFu);
         const int base = ((q0 + t) << 2) - lead;
@@ -1031,6 +1037,17 @@ __device__ __forceinline__ void row_finish(const GvrParams& p, Smem<K, BLOCK>& s
         }
       }
       if (!last) return;
+      if (t == 0) {
+        uint32_t spins = 0;
+        while (load_agent(&hdr->done) < (uint32_t)G) {
+          __builtin_amdgcn_s_sleep(1);
+          if (++spins > p.sync.spins) {
+            atomic_add_agent_nr(p.sync.err, 1u);
+            break;
+          }
+        }
+      }
+      __syncthreads();
       if (!direct) {
         for (uint32_t i0 = 0; i0 < m; i0 += 4 * BLOCK) {
           uint64_t r[4];
