@@ -75,26 +75,17 @@ struct SlotHeader {
 };
 static_assert(sizeof(SlotHeader) == 256, "slot header size");
 
-// Split rescue digits: three levels of 11, 11 and 10 bits over the 32-bit
-// key (one row of 2048 counts per level); the deterministic tie pick over
-// positions keeps four 8-bit levels.
-constexpr int kRescueDigitBits = 11;
-constexpr int kRescueLevels = 3;
-constexpr int kRescueDigitBins = 1 << kRescueDigitBits;
-
 struct SlotFixed {
   SlotHeader hdr;
-  uint32_t rdig[kRescueLevels][kRescueDigitBins];  // rescue digit counts per level
-  uint32_t tdig[4][256];  // the deterministic tie pick's digit counts per level
-  uint32_t hist[2048];    // the row's value histogram (bins >= the floor bin)
+  uint32_t dig[8][256];  // rescue digit counts, one row per radix level
+                         // (rows 4..7: the deterministic tie pick)
+  uint32_t hist[2048];   // the row's value histogram (bins >= the floor bin)
   // Spacing only.  The slots' counters and histograms take atomics from every
   // workgroup of their rows; at a 16640-byte stride eight concurrent slots
-  // measured about 15 % slower than at 17664 (memory-channel collisions), so
-  // the stride keeps 17664's offset within a 16 KiB span.
+  // measured about 15 % slower (memory-channel collisions), at 17664 not.
   uint32_t pad[256];
 };
-static_assert(sizeof(SlotFixed) == 38144, "slot fixed block size");
-static_assert(kRescueDigitBins == kBins, "a second counting round reuses the first digit row");
+static_assert(sizeof(SlotFixed) == 17664, "slot fixed block size");
 
 constexpr size_t kWsHeaderBytes = 256;
 constexpr size_t kWsDataOff = kWsHeaderBytes + sizeof(SlotFixed) * kMaxSlots;

@@ -40,8 +40,8 @@ __device__ __forceinline__ uint32_t rkey(float x) { return (x == x) ? fkey(x) : 
 constexpr int kBufWord3 = 0x00020000;
 // Cache policy of streaming loads: non-temporal (the scores are read once).
 constexpr int kCachePolicyNT = 2;
-// Cache policy of loads of what other workgroups wrote by agent-scope
-// atomics: sc1, as on the compiler's own agent-scope atomic loads.
+// Cache policy of stores that other workgroups read by agent-scope atomic
+// loads: sc1, as on the compiler's own agent-scope atomic stores.
 constexpr int kCachePolicyAgent = 16;
 
 // Raw buffer resource over [p, p + bytes) (p and bytes uniform: both go
@@ -527,32 +527,6 @@ __device__ __forceinline__ void find_crossing(Load&& load, uint32_t target, Cros
   crossing_from<NBINS, BLOCK, PER>(c, target, out, scan_sm);
 }
 
-// find_crossing over NBINS counts in global memory that other workgroups
-// merged by agent-scope atomics (complete before the caller's row barrier):
-// each thread reads its PER consecutive bins as 16-byte loads with the
-// agent-coherent cache policy (the one the compiler gives agent-scope atomic
-// loads), so a wave's load covers one contiguous stretch.
-template <int NBINS, int BLOCK>
-__device__ __forceinline__ void find_crossing_agent(const uint32_t* h, uint32_t target, Cross* out,
-                                                    uint32_t* scan_sm) {
-  constexpr int PER = NBINS / BLOCK;
-  static_assert(PER % 4 == 0 && PER * BLOCK == NBINS, "whole 16-byte groups per thread");
-  const int t = threadIdx.x;
-  const int lo = NBINS - (t + 1) * PER;  // this thread's lowest bin
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(h, NBINS * 4);
-  uint32_t c[PER];
-#pragma unroll
-  for (int v = 0; v < PER / 4; ++v) {
-    const uint4 q = __builtin_bit_cast(
-        uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, (lo + 4 * v) * 4, 0, kCachePolicyAgent));
-    c[PER - 1 - 4 * v] = q.x;
-    c[PER - 2 - 4 * v] = q.y;
-    c[PER - 3 - 4 * v] = q.z;
-    c[PER - 4 - 4 * v] = q.w;
-  }
-  crossing_from<NBINS, BLOCK, PER>(c, target, out, scan_sm);
-}
-
 // The crossing over the kBins-word LDS histogram h with a single workgroup
 // barrier: thread t sums its kBins / BLOCK bins from the top, a wave prefix
 // sum plus the waves' totals (through scan_sm, after the barrier) give every
@@ -713,16 +687,13 @@ __device__ __forceinline__ bool finish_slot(SlotHeader* hdr, int G, uint32_t* bc
 }
 
 // Return a row's slot to its resting state (all zero): the histogram from bin
-// hist_lo up (no round adds below its floor), the first `rrows` rescue digit
-// rows and the first `trows` tie-pick rows (with any of them, the class
-// extremes too), and the header.
-__device__ __forceinline__ void rest_slot(SlotFixed* sf, int t, int block, int hist_lo, int rrows,
-                                          int trows) {
-  for (int i = t; i < rrows * kRescueDigitBins / 4; i += block)
-    reinterpret_cast<uint4*>(&sf->rdig[0][0])[i] = uint4{0u, 0u, 0u, 0u};
-  for (int i = t; i < trows * 256 / 4; i += block)
-    reinterpret_cast<uint4*>(&sf->tdig[0][0])[i] = uint4{0u, 0u, 0u, 0u};
-  if (rrows + trows > 0 && t < 16) sf->hdr.class_ext[t] = 0u;
+// hist_lo up (no round adds below its floor), the digit rows when `dig`, and
+// the header.
+__device__ __forceinline__ void rest_slot(SlotFixed* sf, int t, int block, int hist_lo, bool dig) {
+  if (dig) {
+    for (int i = t; i < 8 * 256; i += block) (&sf->dig[0][0])[i] = 0u;
+    if (t < 16) sf->hdr.class_ext[t] = 0u;
+  }
   for (int i = hist_lo + t; i < kBins; i += block) sf->hist[i] = 0u;
   if (t == 0) {
     sf->hdr.bar_count = 0u;
@@ -778,11 +749,7 @@ __device__ __forceinline__ RSel radix_select(Iter&& iter, uint32_t need, uint32_
     const int hs = shift;  // the digits from bit hs up are fixed
     shift = 32 - DB * (L + 1) > 0 ? 32 - DB * (L + 1) : 0;
     const uint32_t dmask = (2u << (hs - shift - 1)) - 1u;
-    if constexpr (NB >= 4 * BLOCK) {
-      for (int i = t; i < NB / 4; i += BLOCK) reinterpret_cast<uint4*>(dh)[i] = uint4{0u, 0u, 0u, 0u};
-    } else {
-      for (int i = t; i < NB; i += BLOCK) dh[i] = 0u;
-    }
+    for (int i = t; i < NB; i += BLOCK) dh[i] = 0u;
     lds_sync();
     uint32_t kmax = 0u, knmin = 0u;  // the class's largest key, smallest complemented
     iter([&](uint32_t key) {
@@ -831,10 +798,7 @@ __device__ __forceinline__ RSel radix_select(Iter&& iter, uint32_t need, uint32_
         gmx = load_agent(&gext[L]);
         gmn = load_agent(&gext[4 + L]);
       }
-      if constexpr (NB >= 4 * BLOCK)
-        find_crossing_agent<NB, BLOCK>(gd, rem, cross, scan);
-      else
-        find_crossing<NB, BLOCK>([&](int d) { return load_agent(&gd[d]); }, rem, cross, scan);
+      find_crossing<NB, BLOCK>([&](int d) { return load_agent(&gd[d]); }, rem, cross, scan);
       if (EXT) {
         kmax = (uint32_t)__builtin_amdgcn_readfirstlane((int)gmx);
         knmin = (uint32_t)__builtin_amdgcn_readfirstlane((int)gmn);

@@ -18,9 +18,8 @@
 //  5. compact winners to the output and candidates to a buffer;
 //  6. refine: the `need` largest candidates, exactly;
 //  7. rescue when the bracket is invalid or the candidates overflow: an exact
-//     radix select over the whole row's resident keys, using every
-//     workgroup of the row, inside the same launch (4 x 8-bit digits in one
-//     workgroup, 11 + 11 + 10 bits across several; it stops early on a digit
+//     4 x 8-bit radix select over the whole row's resident keys, using every
+//     workgroup of the row, inside the same launch (it stops early on a digit
 //     class that holds one key).
 //
 // Two tiers share the steps:
@@ -47,8 +46,6 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-
-#include <type_traits>
 
 #include "gvr_common.h"
 #include "gvr_device.h"
@@ -297,18 +294,6 @@ __device__ __forceinline__ bool row_begin(const GvrParams& p, Smem<K, BLOCK>& sm
   return true;
 }
 
-// Visit groups J, J + 1, ... while they are below n (uniform): the tests
-// nest, so the first group past n ends the visit with one branch.
-template <int J, int N, class G>
-__device__ __forceinline__ void visit_groups(int n, G&& g) {
-  if constexpr (J < N) {
-    if (J < n) {
-      g(std::integral_constant<int, J>{});
-      visit_groups<J + 1, N>(n, g);
-    }
-  }
-}
-
 // The selection of a row whose loads row_begin issued.
 template <int K, int QPT, int BLOCK, bool SPLIT>
 __device__ __forceinline__ void row_finish(const GvrParams& p, Smem<K, BLOCK>& sm, int g,
@@ -344,12 +329,14 @@ __device__ __forceinline__ void row_finish(const GvrParams& p, Smem<K, BLOCK>& s
     int ll = l, njp = nj, jf0p = jf0, jf1p = jf1;
     asm volatile("" : "+v"(ll));
     asm volatile("" : "+s"(njp));
-    visit_groups<0, QPT>(njp, [&](auto J) {
-      constexpr int j = decltype(J)::value;
-      const int q = qw0 + j * BLOCK + ll;
-      const bool full = j >= jf0p && j < jf1p;
-      f(j, q, full);
-    });
+#pragma unroll
+    for (int j = 0; j < QPT; ++j) {
+      if (j < njp) {
+        const int q = qw0 + j * BLOCK + ll;
+        const bool full = j >= jf0p && j < jf1p;
+        f(j, q, full);
+      }
+    }
   };
   auto resident = [&](auto&& f) {
     each([&](int j, int q, bool) {
@@ -913,15 +900,15 @@ __device__ __forceinline__ void row_finish(const GvrParams& p, Smem<K, BLOCK>& s
         lds_sync();  // every wave has read the merged counts
         for (int i = t; i < kBins + 64; i += BLOCK) sm.u.hist[i] = 0u;
         floor_bin = 0;
-        path = verify(0, &sf->rdig[0][0]);
+        path = verify(0, &sf->dig[0][0]);
         if (path == 1) {
           path = 5;
         } else {
-          // the rescue merges its first level's digit counts in that row:
-          // every workgroup has read it; back to zero, then on
+          // the rescue merges its digit counts in those rows: every
+          // workgroup has read them; back to zero, then on
           row_barrier(hdr, G, nbar, p.sync);
-          for (int i = t; i < kRescueDigitBins; i += BLOCK)
-            __hip_atomic_store(&sf->rdig[0][0] + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          for (int i = t; i < 8 * 256; i += BLOCK)
+            __hip_atomic_store(&sf->dig[0][0] + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           row_barrier(hdr, G, nbar, p.sync);
         }
       }
@@ -1075,8 +1062,8 @@ __device__ __forceinline__ void row_finish(const GvrParams& p, Smem<K, BLOCK>& s
         }
       }
       // back to zero: the histogram bins the first round added to, and the
-      // first digit row when a second round used it
-      rest_slot(sf, t, BLOCK, blo, path == 5 ? 1 : 0, 0);
+      // digit rows when a second round used them
+      rest_slot(sf, t, BLOCK, blo, path == 5);
       put_stats(path, (int)cr.m, (int)cr.above, cr.b);
       return;
     }
@@ -1084,17 +1071,14 @@ __device__ __forceinline__ void row_finish(const GvrParams& p, Smem<K, BLOCK>& s
 
   // ---- rescue (a8): exact radix select over the whole row -----------------
   {
-    // Split, three 11-bit digit levels (each level's merge costs a few
-    // global round trips; the counts sit in the value histogram's LDS, free
-    // by now); one workgroup, four 8-bit levels in LDS.
-    const RSel s = radix_select<BLOCK, true, SPLIT, SPLIT ? kRescueDigitBits : 8>(
-        resident, (uint32_t)K, SPLIT ? sm.u.hist : sm.dh, &sm.cross, sm.scan, sm.mm,
-        SPLIT ? &sf->rdig[0][0] : nullptr, SPLIT ? &hdr->class_ext[0] : nullptr, hdr, G, nbar,
+    const RSel s = radix_select<BLOCK, true, SPLIT>(
+        resident, (uint32_t)K, sm.dh, &sm.cross, sm.scan, sm.mm,
+        SPLIT ? &sf->dig[0][0] : nullptr, SPLIT ? &hdr->class_ext[0] : nullptr, hdr, G, nbar,
         p.sync);
     // Deterministic mode: when the K-th key's class holds more scores than
     // are needed, keep its smallest positions -- a second radix select over
     // the class's complemented positions (other scores count as key 0; the
-    // row's workgroups merge through the tie-pick digit rows).  Positions are
+    // row's workgroups merge through digit rows 4..7).  Positions are
     // distinct, so that select always ends with its last digit class needed
     // whole: the choice takes no ticket.
     const bool pick = p.deterministic && s.cnt > s.rem;
@@ -1113,7 +1097,7 @@ __device__ __forceinline__ void row_finish(const GvrParams& p, Smem<K, BLOCK>& s
               }
             });
           },
-          s.rem, sm.dh, &sm.cross, sm.scan, sm.mm, SPLIT ? &sf->tdig[0][0] : nullptr,
+          s.rem, sm.dh, &sm.cross, sm.scan, sm.mm, SPLIT ? &sf->dig[4][0] : nullptr,
           SPLIT ? &hdr->class_ext[8] : nullptr, hdr, G, nbar, p.sync);
     }
     // a score of the K-th key's class is taken when the tie pick keeps it
@@ -1164,7 +1148,7 @@ __device__ __forceinline__ void row_finish(const GvrParams& p, Smem<K, BLOCK>& s
     bool last = true;
     if (SPLIT) {
       last = finish_slot(hdr, G, &sm.bc[2]);
-      if (last) rest_slot(sf, t, BLOCK, 0, s.levels, pick ? s2.levels : 0);
+      if (last) rest_slot(sf, t, BLOCK, 0, true);
     }
     if (last)
       put_stats(path, bracket_ok && !SPLIT ? (int)cr.m : -1, bracket_ok && !SPLIT ? (int)cr.above : -1,

@@ -9,6 +9,7 @@ wave visits one group fewer than its neighbours."""
 import numpy as np
 import pytest
 
+import oracle
 import workloads
 from gpu_helpers import assert_parity, log, run_gpu
 
@@ -71,3 +72,33 @@ def test_leads_with_many_rows(ert, k):
     log(f"[windows] many rows k={k}")
     got = run_gpu(w)
     assert_parity(w, got)
+
+
+@pytest.mark.parametrize("dist", ["signed_zero", "two_valued"])
+def test_split_rescue_repeated_calls(ert, dist):
+    # Tie-heavy windows whose tie class barely exceeds what is needed (a
+    # wrong count anywhere in the row's merged digit counts moves the
+    # threshold) through the split rescue, many calls in a row on the same
+    # workspace: every call must match the oracle and leave the slots at rest.
+    import torch
+    k, stride = 2048, STRIDE["g17"]
+    starts, ends = [], []
+    for lead in range(4):
+        for base in (0, 64):
+            s = base + lead
+            for n in _lengths(k, stride - s):
+                starts.append(s)
+                ends.append(s + n)
+    w = workloads.random_prefill(starts, ends, stride, k, seed=11, dist=dist)
+    dev = {"logits": torch.from_numpy(np.ascontiguousarray(w.logits)).cuda(),
+           "row_starts": torch.from_numpy(np.ascontiguousarray(w.row_starts)).cuda(),
+           "row_ends": torch.from_numpy(np.ascontiguousarray(w.row_ends)).cuda()}
+    want = oracle.topk_workload(w)
+    log(f"[windows] repeated split rescue {dist} rows={w.num_rows}")
+    for rep in range(24):
+        out = torch.full((w.num_rows, k), -7, dtype=torch.int32, device="cuda")
+        ert.topk_prefill(dev["logits"], dev["row_starts"], dev["row_ends"], k, indices=out,
+                         force_wgs_per_row=4)
+        torch.cuda.synchronize()
+        bad = oracle.check_rows(w, out.cpu().numpy(), want)
+        assert not bad, f"call {rep}: {len(bad)} bad rows, first {bad[:3]}"
