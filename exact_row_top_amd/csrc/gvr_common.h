@@ -54,8 +54,9 @@ constexpr int kBskMaxBlocks = 8192;  // rows the streaming pass takes: <= this m
 //   [0, 256)                             header (unused)
 //   kMaxSlots fixed blocks of 17664 bytes: SlotHeader, digit counts [8][256],
 //   value histogram [kBins]
-//   then one data block per slot: G slices of kBins suffix counts (slice g:
-//   workgroup g's count of scores in bins >= b), then the crossing bin's
+//   then one data block per slot: G slices of kBins 16-bit suffix counts
+//   (slice g: workgroup g's count of scores in bins >= b; a part holds fewer
+//   than 2^16 scores), then the crossing bin's
 //   members as (key, index) pairs [kSingleCap]
 // The fixed blocks hold every word that carries state between workgroups, and
 // the last workgroup of a row returns them all to zero; their place does not
@@ -90,8 +91,8 @@ static_assert(sizeof(SlotFixed) == 17664, "slot fixed block size");
 constexpr size_t kWsHeaderBytes = 256;
 constexpr size_t kWsDataOff = kWsHeaderBytes + sizeof(SlotFixed) * kMaxSlots;
 // Per-slot data block of a plan with G workgroups per row: G slices of
-// kBins suffix counts (one per workgroup), then the member list.
-constexpr size_t kSliceBytes = sizeof(uint32_t) * kBins;
+// kBins 16-bit suffix counts (one per workgroup), then the member list.
+constexpr size_t kSliceBytes = sizeof(uint16_t) * kBins;
 constexpr size_t kListBytes = 2 * sizeof(uint32_t) * kSingleCap;
 constexpr size_t slot_data_bytes(int G) { return (size_t)G * kSliceBytes + kListBytes; }
 constexpr size_t ws_bytes_for(int slots, int G) {

@@ -117,7 +117,7 @@ struct RowCtx {
   int32_t* stats;
   SlotFixed* sf;
   SlotHeader* hdr;
-  uint32_t* slices;
+  uint16_t* slices;
   uint2* s_pair;
   const int32_t* hrow;
 };
@@ -167,13 +167,13 @@ __device__ __forceinline__ bool row_begin(const GvrParams& p, Smem<K, BLOCK>& sm
 
   SlotFixed* sf = nullptr;
   SlotHeader* hdr = nullptr;
-  uint32_t* slices = nullptr;  // per-workgroup suffix counts [G][kBins]
+  uint16_t* slices = nullptr;  // per-workgroup 16-bit suffix counts [G][kBins]
   uint2* s_pair = nullptr;     // crossing-bin members (key, index)
   if (SPLIT) {
     sf = reinterpret_cast<SlotFixed*>(p.ws + kWsHeaderBytes) + slot;
     hdr = &sf->hdr;
     unsigned char* data = p.ws + kWsDataOff + (size_t)slot * slot_data_bytes(G);
-    slices = reinterpret_cast<uint32_t*>(data);
+    slices = reinterpret_cast<uint16_t*>(data);
     s_pair = reinterpret_cast<uint2*>(data + (size_t)G * kSliceBytes);
   }
 
@@ -314,7 +314,7 @@ __device__ __forceinline__ void row_finish(const GvrParams& p, Smem<K, BLOCK>& s
   int32_t* const stats = c.stats;
   SlotFixed* const sf = c.sf;
   SlotHeader* const hdr = c.hdr;
-  uint32_t* const slices = c.slices;
+  uint16_t* const slices = c.slices;
   uint2* const s_pair = c.s_pair;
   const int32_t* const hrow = c.hrow;
   (void)NSB;
@@ -784,9 +784,11 @@ __device__ __forceinline__ void row_finish(const GvrParams& p, Smem<K, BLOCK>& s
       lds_sync();
       {
         // suffix counts: thread t owns PER consecutive bins from the top and
-        // writes them as 16-byte words (whole lines per wave) with the
-        // agent-coherent cache policy; groups wholly below the floor are
-        // skipped (nothing reads a slice below the crossing bin)
+        // writes them as 16-bit counts, four to an 8-byte word (whole lines
+        // per wave), with the agent-coherent cache policy; groups wholly
+        // below the floor are skipped (nothing reads a slice below the
+        // crossing bin)
+        static_assert(BLOCK * QPT * 4 < 65536, "a part's counts fit 16 bits");
         constexpr int PER = kBins / BLOCK;
         const int hi = kBins - 1 - t * PER;
         uint32_t c[PER];
@@ -798,7 +800,7 @@ __device__ __forceinline__ void row_finish(const GvrParams& p, Smem<K, BLOCK>& s
         }
         uint32_t tot;
         uint32_t run = block_excl_scan<BLOCK>(sum, sm.scan, tot);
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(slices + (size_t)g * kBins, kBins * 4);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(slices + (size_t)g * kBins, kBins * 2);
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
           run += c[i];
@@ -809,19 +811,19 @@ __device__ __forceinline__ void row_finish(const GvrParams& p, Smem<K, BLOCK>& s
           for (int q4 = 0; q4 < PER / 4; ++q4) {
             const int b0 = hi - PER + 1 + 4 * q4;  // the group's lowest bin
             if (b0 + 3 >= bl) {
-              typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-              const v4u sv = {c[PER - 1 - 4 * q4], c[PER - 2 - 4 * q4], c[PER - 3 - 4 * q4],
-                              c[PER - 4 - 4 * q4]};
-              __builtin_amdgcn_raw_buffer_store_b128(sv, rs, b0 * 4, 0, kCachePolicyAgent);
+              typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+              const v2u sv = {c[PER - 1 - 4 * q4] | (c[PER - 2 - 4 * q4] << 16),
+                              c[PER - 3 - 4 * q4] | (c[PER - 4 - 4 * q4] << 16)};
+              __builtin_amdgcn_raw_buffer_store_b64(sv, rs, b0 * 2, 0, kCachePolicyAgent);
             }
           }
         } else {
           // (no split part runs more than 512 threads)
-          uint32_t* mine = slices + (size_t)g * kBins;
+          uint16_t* mine = slices + (size_t)g * kBins;
 #pragma unroll
           for (int i = 0; i < PER; ++i)
             if (hi - i >= bl)
-              __hip_atomic_store(&mine[hi - i], c[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              __hip_atomic_store(&mine[hi - i], (uint16_t)c[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         // the row's histogram: one bin per lane, consecutive across a wave
         for (int b = t; b < kBins; b += BLOCK) {
@@ -926,7 +928,7 @@ __device__ __forceinline__ void row_finish(const GvrParams& p, Smem<K, BLOCK>& s
       } else if (w == 2) {
         uint32_t s0 = 0u, s1 = 0u;
         if (l < g) {
-          const uint32_t* sl = slices + (size_t)l * kBins;
+          const uint16_t* sl = slices + (size_t)l * kBins;
           if (cr.b + 1 < kBins)
             s1 = __hip_atomic_load(&sl[cr.b + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           s0 = __hip_atomic_load(&sl[cr.b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

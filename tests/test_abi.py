@@ -102,7 +102,7 @@ def test_workspace_layout():
     assert lay["header_bytes"] == 256 and lay["slots"] == 256
     assert lay["slot_fixed_bytes"] % 256 == 0
     assert lay["data_offset"] == lay["header_bytes"] + lay["slots"] * lay["slot_fixed_bytes"]
-    assert lay["slice_bytes"] == 4 * 2048       # one suffix count per bin
+    assert lay["slice_bytes"] == 2 * 2048       # one 16-bit suffix count per bin
     assert lay["list_bytes"] >= 8 * 2048        # the crossing bin's members, (key, index)
     p = ert.plan_query(64, 131072, 2048)
     per_slot = p["wgs_per_row"] * lay["slice_bytes"] + lay["list_bytes"]
