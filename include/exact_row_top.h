@@ -361,7 +361,8 @@ int topk_device_query(int64_t* out);
  * every word rests at zero between calls), out[2] = slots, out[3] = byte
  * offset of the per-slot data blocks; a plan with G workgroups per row has
  * data blocks of G * out[4] + out[5] bytes (out[4] = one workgroup's slice of
- * suffix counts, out[5] = the crossing-bin member list).  Returns a status. */
+ * suffix counts, one 16-bit count per value bin; out[5] = the crossing-bin
+ * member list).  Returns a status. */
 int topk_workspace_layout(int64_t* out);
 
 /* Measurement aid (not a selection): reads exactly the scores the selection
